@@ -59,6 +59,16 @@ def exact_dot_f32(t_row: np.ndarray, x: np.ndarray) -> np.float32:
     return _f32_round_fraction(q)
 
 
+def _exponent_span(a: np.ndarray, axis: int) -> np.ndarray:
+    """max - min of the binary exponents of the non-zero entries along axis
+    (0 when there are fewer than two non-zero entries)."""
+    _, e = np.frexp(a)
+    nz = a != 0
+    hi = np.where(nz, e, -100000).max(axis=axis)
+    lo = np.where(nz, e, 100000).min(axis=axis)
+    return np.maximum(hi - lo, 0)
+
+
 def transform_ref(x_bits: np.ndarray, t_bits: np.ndarray, return_abs: bool = False):
     """y[m, cG + k] = fp32( sum_j T[c][k][j] * X[m, cG + j] ), exact sum.
 
@@ -67,10 +77,16 @@ def transform_ref(x_bits: np.ndarray, t_bits: np.ndarray, return_abs: bool = Fal
     ``return_abs`` it also returns A = sum_j |T[c][k][j] x_j| (float64), which
     bounds the rounding error of any fp32 accumulation order.
 
-    Method: every bf16 x bf16 product is exact in float64.  The float64 matmul
-    then has error at most E = 2**-47 * A.  Wherever [S - E, S + E] rounds to
-    a single fp32 value, that value is the correctly rounded exact sum.  The
-    few elements where it does not are recomputed in exact rationals.
+    Method.  A bf16 value has an 8-bit significand, so each product has at
+    most 16 significant bits and is exact in float64.  Suppose the products'
+    exponents span s octaves.  Then every partial sum is a multiple of the
+    smallest product's last bit, and stays below 32 times the largest
+    product.  That needs s + 21 bits.  So the float64 sum, in any order, is
+    exact when s <= 32, and one cast to fp32 rounds it correctly.  The span
+    is bounded by span(x) + span(T row).  For the remaining elements the
+    float64 error is below E = 2**-47 * A.  If [S - E, S + E] rounds to a
+    single fp32 value, that value is the answer.  Otherwise the element is
+    recomputed in exact rationals.
     """
     M, K = x_bits.shape
     C, G, G2 = t_bits.shape
@@ -79,14 +95,20 @@ def transform_ref(x_bits: np.ndarray, t_bits: np.ndarray, return_abs: bool = Fal
     X = codecs.bf16_bits_to_f32(x_bits).astype(np.float64).reshape(M, C, G).transpose(1, 0, 2)
     T = codecs.bf16_bits_to_f32(t_bits).astype(np.float64)
     S = np.matmul(X, T.transpose(0, 2, 1))  # [C, M, G]
-    A = np.matmul(np.abs(X), np.abs(T).transpose(0, 2, 1))
-    E = A * 2.0 ** -47 + np.abs(S) * 2.0 ** -52
-    lo = (S - E).astype(np.float32)
-    hi = (S + E).astype(np.float32)
     y = S.astype(np.float32)
-    bad = np.argwhere(lo != hi)
-    for c, m, k in bad:
-        y[c, m, k] = exact_dot_f32(T[c, k], X[c, m])
+    exact = (_exponent_span(X, 2)[:, :, None] + _exponent_span(T, 2)[:, None, :]) <= 32
+    A = None
+    if return_abs or not exact.all():
+        A = np.matmul(np.abs(X), np.abs(T).transpose(0, 2, 1))
+    if not exact.all():
+        c_i, m_i, k_i = np.nonzero(~exact)
+        s_ = S[c_i, m_i, k_i]
+        e_ = A[c_i, m_i, k_i] * 2.0 ** -47 + np.abs(s_) * 2.0 ** -52
+        lo = (s_ - e_).astype(np.float32)
+        hi = (s_ + e_).astype(np.float32)
+        for j in np.nonzero(lo != hi)[0]:
+            c, m, k = c_i[j], m_i[j], k_i[j]
+            y[c, m, k] = exact_dot_f32(T[c, k], X[c, m])
     y[y == 0] = 0.0  # an exactly-zero sum is +0
     y = np.ascontiguousarray(y.transpose(1, 0, 2).reshape(M, K))
     if return_abs:

@@ -128,13 +128,15 @@ def test_transform_double_rounding_case():
     the 2^-80 term and then lands on the tie, which would round down to 1."""
     G = 32
     x = np.zeros((1, G))
-    x[0, :3] = [1.0, 2.0 ** -24, 2.0 ** -80]
+    x[0, :4] = [1.0, 2.0 ** -24, 2.0 ** -80, 2.0 ** -54]
     T = np.zeros((1, G, G))
     T[0, 0, :3] = 1.0
     T[0, 1, :3] = [1.0, 1.0, -1.0]  # just below the midpoint: rounds down
+    T[0, 2, [0, 1, 3]] = 1.0  # span 54: float64 also drops the last term
     y = quant.transform_ref(_bits(x), _bits(T))
     assert y[0, 0] == np.float32(1.0 + 2.0 ** -23)
     assert y[0, 1] == np.float32(1.0)
+    assert y[0, 2] == np.float32(1.0 + 2.0 ** -23)
 
 
 def test_transform_cyclic_shift_not_transposed():
