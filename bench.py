@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused WUSH transform + MXFP4 quantization on one MI355X.
+
+One step is one pass of the whole online path over one batch: every token's
+bf16 row is transformed block by block with T_wush and quantized to E2M1
+codes plus E8M0 scales.  That is one wush_quant_mxfp4 call on the
+4096-token x 4096-channel workload (G = 32, 128 blocks, Student-t(3)
+activations with 1% outlier channels).  The inputs are synthetic, seeded, and
+resident in HBM before the timed region starts.
+
+Metric: algorithmic HBM bytes per step (X read once, T once, codes and
+scales written once) divided by the time per step, in GB/s.  Cold cache:
+the steps rotate through buffer sets whose total footprint is more than
+twice the 256 MB Infinity Cache, so each step reads its inputs from HBM.
+
+Printed: one JSON line.  It carries the roofline of the kernel (average
+kernel duration from HIP events around each launch), and the CPU oracle
+timed on the host as a reported baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MALL_BYTES = 256 << 20
+
+
+def algorithmic_bytes(fmt: str, M: int, K: int, G: int) -> int:
+    scale_bytes = 2 if fmt == "int4" else 1
+    return M * K * 2 + M * K // 2 + M * (K // G) * scale_bytes + (K // G) * G * G * 2
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=320)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", default="llama8b_mxfp4",
+                    help="llama8b_mxfp4 (default), downproj_mxfp4, nvfp4, int4, tiny_mxfp4")
+    ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: > 2x MALL)")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the path, run a plain device copy of this many MiB --steps times "
+                         "(reference for the HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_probe(mib: int, steps: int) -> None:
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "steps": steps,
+                      "ms_per_copy": round(ms, 6), "GBps_read_plus_write": round(2 * n / ms / 1e6, 2)}),
+          flush=True)
+
+
+def cpu_baseline(wl, x_bits_np, t_bits_np, seconds: float):
+    """The oracle as it stands, on the host cores, over whole passes of the
+    same workload until at least `seconds` have elapsed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import quant
+
+    cores = len(os.sched_getaffinity(0))
+    g = None
+    passes = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        while True:
+            if wl.fmt == "nvfp4" and g is None:
+                y = quant.transform_ref(x_bits_np, t_bits_np)
+                g = quant.nvfp4_global_scale(quant.tensor_amax_ref(y))
+            quant.run_path(wl.fmt, x_bits_np, t_bits_np, g)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    nbytes = algorithmic_bytes(wl.fmt, wl.M, wl.K, wl.G)
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    del np
+    return {
+        "value": round(nbytes * passes / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d full pass(es) of the %dx%d workload in %.1f s (NumPy float64 oracle, "
+                  "BLAS threads=%d, rest single-threaded; %s)" % (passes, wl.M, wl.K, el, cores, cpu_model),
+        "elements_per_s": round(wl.M * wl.K * passes / el, 1),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the path needs no cross-GPU exchange (token rows are "
+              "independent), so --gpus must be 1 (got --gpus %d, WORLD_SIZE %d)." % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, args.steps)
+        return
+
+    import numpy as np
+    import torch
+
+    import mxfp4_activation_amd as wush
+    from mxfp4_activation_amd import _lib, transforms
+    from synthetic import CONFIGS, gen_calibration, gen_weight, gen_x_bits
+
+    wl = CONFIGS[args.workload]
+    M, K, G, fmt = wl.M, wl.K, wl.G, wl.fmt
+    lib = wush.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("bench: workload %s (%s, M=%d, K=%d, G=%d)" % (wl.name, fmt, M, K, G), file=sys.stderr, flush=True)
+
+    # Inputs: seeded activations and the offline transform bank.
+    x_np = gen_x_bits(wl)
+    Tw, _ = transforms.wush_transforms(torch.from_numpy(gen_weight(wl)), torch.from_numpy(gen_calibration(wl)), G)
+    T_bf16 = transforms.to_kernel_layout(Tw)
+    t_np = T_bf16.view(torch.int16).numpy().view(np.uint16)
+    X0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    T0 = T_bf16.to(dev)
+
+    nbytes = algorithmic_bytes(fmt, M, K, G)
+    per_set = nbytes
+    n_sets = args.sets or max(2, -(-2 * MALL_BYTES // per_set) + 1)
+    sets = []
+    sdt = torch.float16 if fmt == "int4" else torch.uint8
+    for i in range(n_sets):
+        X = X0.clone() if i else X0
+        T = T0.clone() if i else T0
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((M, K // G), dtype=sdt, device=dev)
+        sets.append((X, T, codes, scales))
+    gscale = torch.zeros(1, dtype=torch.float32, device=dev)
+    if fmt == "nvfp4":
+        wush.nvfp4_global_scale(X0, T0, out=gscale)
+    torch.cuda.synchronize()
+
+    fmt_id = _lib.FMT[fmt]
+    gs_ptr = gscale.data_ptr() if fmt == "nvfp4" else None
+    ptrs = [(X.data_ptr(), T.data_ptr(), c.data_ptr(), s.data_ptr()) for X, T, c, s in sets]
+    quant_fn = lib.wush_quant
+
+    def launch(i):
+        xp, tp, cp, sp = ptrs[i % n_sets]
+        st = quant_fn(fmt_id, xp, tp, M, K, gs_ptr, cp, sp, None, torch.cuda.current_stream().cuda_stream)
+        if st:
+            _lib.check(st, "wush_quant")
+
+    # Warmup: W untimed steps.
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+
+    # Per-launch kernel durations from HIP events on the launch stream.
+    # These give the kernel's average duration for the roofline.
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        launch(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    # Timed region: exactly K steps back to back.  In graph mode the steps
+    # are replayed from HIP graphs (one rotation over the buffer sets per
+    # graph), so host launch cost does not gate the device.
+    graphs = []
+    if args.mode == "graph":
+        cap = torch.cuda.Stream()
+        full, rem = divmod(args.steps, n_sets)
+
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(n):
+                    launch(i)
+            return g
+
+        g_full = capture(n_sets) if full else None
+        g_rem = capture(rem) if rem else None
+        # one untimed replay of each graph uploads it (not counted as a step)
+        for g in (g_full, g_rem):
+            if g is not None:
+                g.replay()
+        torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    if args.mode == "graph":
+        for _ in range(full):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
+    else:
+        for i in range(args.steps):
+            launch(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    kern_avg_ms = float(kern_ms.mean())
+    achieved = nbytes / (kern_avg_ms * 1e-3) / 1e9
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name)
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha") == _kernel_source_sha():
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    out = {
+        "metric": "fused WUSH+%s quant: HBM GB/s and %% of peak at d=%d, %d tokens" % (fmt.upper(), K, M),
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: X bf16 [%d x %d], G=%d, %s, %d outlier channels x%g; T_wush per block from "
+                        "W [%d x %d] N(0,0.02) and %d calibration tokens" % (
+                            wl.name, M, K, G, wl.dist, wl.n_outlier, wl.outlier_mult, wl.d_out, K, wl.n_cal),
+            "format": fmt,
+            "tokens": M,
+            "d": K,
+            "G": G,
+            "algorithmic_bytes_per_step": nbytes,
+            "cold_cache_sets": n_sets,
+            "timing": args.mode,
+            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "elements_per_s": round(M * K / (ms_per_step * 1e-3), 1),
+            "host_wall_s": round(wall, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "quant_kernel<%s>" % fmt,
+            "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
+            "kernel_p10_p90_us": [round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
+                                  round(float(np.percentile(kern_ms, 90)) * 1e3, 3)],
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle (~%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, x_np, t_np, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def _kernel_source_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in ("wush_kernels.hip", "wush_kernels.h", "wush_abi.cpp"):
+        with open(os.path.join(ROOT, "mxfp4_activation_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,140 @@
+/*
+ * wush.h -- C ABI of the WUSH online activation path on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation comes from "WUSH: Near-Optimal Adaptive Transforms for LLM
+ * Quantization" (arXiv 2512.00956).  Each token's activation row is cut into
+ * blocks of G contiguous channels.  Each block is multiplied by its own G x G
+ * matrix T_wush(c) = H S^-1/2 U^T W'^T, built offline (Eq. 8; deep dive,
+ * section 3.4.4).  The result is quantized round-to-nearest with an AbsMax
+ * scale per group of G (deep dive, sections 3.4.6 and 3.4.7; Eq. 10).  The
+ * transform and the quantization run in one kernel pass, so the transformed
+ * activations never go to memory (deep dive, section 3.4.7, "QuTLASS
+ * baseline" paragraph).
+ *
+ * Conventions for every entry point:
+ *   - Every buffer is a DEVICE pointer on the current HIP device, allocated
+ *     and owned by the caller.  The library allocates no memory, keeps no
+ *     state that changes between calls, and is thread-safe.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call
+ *     returns without synchronizing.  Results are visible to later work on
+ *     that stream.
+ *   - Arguments are validated before any HIP call.  If validation fails,
+ *     nothing is launched and the matching error code is returned;
+ *     wush_last_error() then holds a message, per thread.
+ *   - M == 0 is a valid no-op that returns WUSH_OK.
+ *   - Inputs must be finite.  NaN and Inf inputs are outside the contract.
+ *   - Device faults surface at the caller's next synchronization, not here.
+ *
+ * Layouts (all row-major):
+ *   X       bf16 [M][K].  Token m, channel k at X[m*K + k].  16-byte aligned.
+ *   T       bf16 [K/G][G][G].  T[c][i][j] multiplies x_(cG+j) into output i of
+ *           block c, so block c's matrix is one contiguous G*G slice.
+ *           16-byte aligned.
+ *   codes   uint8 [M][K/2].  Element 2j in bits 3:0 of byte j, element 2j+1
+ *           in bits 7:4.  8-byte aligned.
+ *   scales  one per (token, block), [M][K/G].  The format decides the type.
+ *
+ * Pre-quantization values: y = fp32 rounding of the exact sum
+ * sum_j T[c][i][j] * x_j.  The kernels use fp32 matrix-core accumulation,
+ * which can differ from the exact sum by an error bounded by the sum of
+ * |T x| terms.  Any group whose scale decision falls within that bound of
+ * a rounding boundary is recomputed in float64.  So every scale equals the
+ * one computed from the exactly rounded y.  An element code may still differ
+ * by one level where the scaled value sits within that bound of a rounding
+ * midpoint.
+ */
+#ifndef WUSH_H_
+#define WUSH_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WUSH_ABI_VERSION 1
+
+typedef enum wush_status {
+  WUSH_OK = 0,
+  WUSH_EINVAL = 1,       /* bad size, null pointer or overlapping buffers   */
+  WUSH_EALIGN = 2,       /* a pointer does not meet its alignment           */
+  WUSH_EUNSUPPORTED = 3, /* current device is not gfx950, or bad G/format   */
+  WUSH_EHIP = 4          /* HIP runtime error (launch or device query)      */
+} wush_status;
+
+/* MXFP4 (G = 32).  E2M1 codes, rounded to nearest even with saturation at 6.
+ * One E8M0 scale byte per 32: code = e + 127, where e = floor(log2 amax) - 2
+ * clamped to [-127, 127], and amax = 0 gives code 0.  Elements are y * 2^-e.
+ * MXFP4 is E2M1 elements with a shared 8-bit scale per 32 (deep dive,
+ * section 2, "New block-level floating-point formats"; OCP MX v1.0).
+ * scales: uint8 [M][K/32].  K must be a multiple of 32. */
+wush_status wush_quant_mxfp4(const void* X, const void* T, int64_t M, int64_t K,
+                             void* codes, void* scales, hipStream_t stream);
+
+/* NVFP4 (G = 16).  E2M1 codes.  One OCP E4M3FN scale byte per 16, relative to
+ * a per-tensor fp32 scale g read from device memory at `global_scale`:
+ *   code = E4M3_rne_sat(fp32(fp32(amax/6) / g)),  eff = E4M3(code) * g,
+ *   elements = y * fp32(1/eff).
+ * If g == 0 or eff == 0, the group's codes are all zero.  Pass the g from
+ * wush_nvfp4_global_scale (dynamic) or a calibrated constant (static).  g
+ * must be 0 or at least 2^-100.  NVFP4 is E2M1 with an FP8 scale per 16 (deep
+ * dive, section 2).
+ * scales: uint8 [M][K/16].  K must be a multiple of 16. */
+wush_status wush_quant_nvfp4(const void* X, const void* T, int64_t M, int64_t K,
+                             const float* global_scale, void* codes, void* scales,
+                             hipStream_t stream);
+
+/* INT4 (G = 32).  Symmetric levels -7..7, stored as two's-complement nibbles.
+ * One IEEE fp16 scale per 32: s = fp16(fp32(amax / 7)).  Elements are
+ * rne(clamp(y * fp32(1/s), -7, 7)), and s == 0 gives zero codes.  This is
+ * the AbsMax INT quantizer (deep dive, section 3.4.5).
+ * scales: fp16 bits [M][K/32], 2-byte aligned.  K must be a multiple of 32. */
+wush_status wush_quant_int4(const void* X, const void* T, int64_t M, int64_t K,
+                            void* codes, void* scales, hipStream_t stream);
+
+/* Generic form of the three entry points above.
+ * fmt: 0 = MXFP4, 1 = NVFP4, 2 = INT4.
+ * global_scale: used only for NVFP4.
+ * n_exact: if non-null, a device uint32 to which the kernel atomically adds
+ * the number of groups it recomputed in float64.  The caller zeroes it. */
+wush_status wush_quant(int fmt, const void* X, const void* T, int64_t M, int64_t K,
+                       const float* global_scale, void* codes, void* scales,
+                       uint32_t* n_exact, hipStream_t stream);
+
+/* Transform only: Y[m][cG+i] = sum_j T[c][i][j] x_(cG+j), in fp32 from the
+ * matrix cores, without rounding fix-up.  G is 16 or 32.  Use it to check
+ * values before quantization, or when the transformed activations are wanted
+ * in fp32.
+ * Y: fp32 [M][K], 16-byte aligned. */
+wush_status wush_transform_f32(const void* X, const void* T, int64_t M, int64_t K, int G,
+                               float* Y, hipStream_t stream);
+
+/* Largest |y| over the whole transformed tensor (fp32, matrix-core values).
+ * *amax is overwritten, not accumulated.  G is 16 or 32. */
+wush_status wush_transformed_absmax(const void* X, const void* T, int64_t M, int64_t K, int G,
+                                    float* amax, hipStream_t stream);
+
+/* NVFP4 per-tensor scale: *global_scale = fp32(absmax(T x) / 2688), with
+ * 2688 = 6 * 448.  The block holding the tensor maximum then gets the
+ * largest E4M3 scale.  G = 16. */
+wush_status wush_nvfp4_global_scale(const void* X, const void* T, int64_t M, int64_t K,
+                                    float* global_scale, hipStream_t stream);
+
+/* The E2M1 element rounding the kernels use, exposed for exhaustive testing:
+ * codes[i] = E2M1_rne_sat(v[i]), one 4-bit code per byte, sign in bit 3.
+ * n >= 0.  v is fp32, 4-byte aligned. */
+wush_status wush_e2m1_encode(const float* v, int64_t n, uint8_t* codes, hipStream_t stream);
+
+/* Status text, and the detail of the last failure on this thread. */
+const char* wush_status_string(wush_status status);
+const char* wush_last_error(void);
+int wush_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WUSH_H_ */

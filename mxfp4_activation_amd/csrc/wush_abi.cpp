@@ -1,0 +1,278 @@
+// C-ABI layer of the WUSH online path.  It validates arguments, checks the
+// device, picks the launch shape and forwards to the kernels.
+// Contract: include/wush.h.
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/wush.h"
+#include "wush_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+wush_status fail(wush_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Half-open byte ranges [p, p + n) overlap?
+bool overlap(const void* p, uint64_t np, const void* q, uint64_t nq) {
+  if (!p || !q || np == 0 || nq == 0) return false;
+  uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + nq && b < a + np;
+}
+
+// Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_ok[kMaxDevices];
+
+wush_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(WUSH_EUNSUPPORTED, "device index %d out of range", dev);
+  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(WUSH_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(WUSH_EUNSUPPORTED, "device %d is not gfx950", dev);
+  return WUSH_OK;
+}
+
+// Shape checks common to every entry point that reads X and T.
+wush_status check_shape(const void* X, const void* T, int64_t M, int64_t K, int G) {
+  if (G != 16 && G != 32) return fail(WUSH_EUNSUPPORTED, "G must be 16 or 32 (got %d)", G);
+  if (M < 0) return fail(WUSH_EINVAL, "M must be >= 0 (got %lld)", (long long)M);
+  if (K <= 0 || K % G != 0) return fail(WUSH_EINVAL, "K must be a positive multiple of %d (got %lld)", G, (long long)K);
+  if (K > (int64_t)1 << 30) return fail(WUSH_EINVAL, "K too large (%lld)", (long long)K);
+  if (M > (INT64_MAX / 4) / K) return fail(WUSH_EINVAL, "M*K overflows");
+  if (M == 0) return WUSH_OK;
+  if (!X || !T) return fail(WUSH_EINVAL, "null X or T");
+  if (!aligned(X, 16) || !aligned(T, 16)) return fail(WUSH_EALIGN, "X and T must be 16-byte aligned");
+  return WUSH_OK;
+}
+
+// Work split: each wave owns one 32-channel panel and walks a run of
+// 32-token tiles.  Runs are sized so that the grid holds at least ~4
+// workgroups per CU when the problem allows, and a wave reuses its T
+// fragment over up to 8 tiles.
+void plan(int64_t M, int64_t K, int64_t* n_tiles, int64_t* tpw, int* n_panels, int* n_pg, int* n_tg) {
+  *n_tiles = (M + 31) / 32;
+  *n_panels = (int)((K + 31) / 32);
+  *n_pg = (*n_panels + wush::kWavesPerGroup - 1) / wush::kWavesPerGroup;
+  const int64_t target_wg = 1024;  // 256 CUs x 4
+  int64_t t = 8;
+  while (t > 1 && (int64_t)(*n_pg) * ((*n_tiles + t - 1) / t) < target_wg) t >>= 1;
+  *tpw = t;
+  *n_tg = (int)((*n_tiles + t - 1) / t);
+}
+
+// Quant kernel split: a workgroup owns a 32-token x 256-channel tile
+// column (kPanelsPerTile panels) and walks a run of 32-token tiles down it.
+// Runs are as long as possible while the grid still gives every CU about
+// 4 workgroups (256 CUs).  Longer runs amortize the T fragment loads and
+// let the next tile's loads overlap the current tile's compute.
+// WUSH_TILES_PER_WG overrides the run length (1..64) for tuning.
+void plan_quant(int64_t M, int64_t K, int64_t* n_tiles, int64_t* tpw, int* n_panels, int* n_pg, int* n_tg) {
+  *n_tiles = (M + 31) / 32;
+  *n_panels = (int)((K + 31) / 32);
+  *n_pg = (*n_panels + wush::kPanelsPerTile - 1) / wush::kPanelsPerTile;
+  const int64_t target_wg = 1024;
+  int64_t t = 16;
+  while (t > 1 && (int64_t)(*n_pg) * ((*n_tiles + t - 1) / t) < target_wg) t >>= 1;
+  static const int64_t env = [] {
+    const char* s = getenv("WUSH_TILES_PER_WG");
+    return s ? (int64_t)atoll(s) : (int64_t)0;
+  }();
+  if (env >= 1 && env <= 64) t = env;
+  *tpw = t;
+  *n_tg = (int)((*n_tiles + t - 1) / t);
+}
+
+int64_t env_tpw() {
+  static int64_t v = [] {
+    const char* s = getenv("WUSH_TILES_PER_WAVE");
+    return s ? (int64_t)atoll(s) : (int64_t)0;
+  }();
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wush_status_string(wush_status s) {
+  switch (s) {
+    case WUSH_OK: return "ok";
+    case WUSH_EINVAL: return "invalid argument";
+    case WUSH_EALIGN: return "misaligned pointer";
+    case WUSH_EUNSUPPORTED: return "unsupported device or parameter";
+    case WUSH_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* wush_last_error(void) { return g_last_error; }
+
+int wush_abi_version(void) { return WUSH_ABI_VERSION; }
+
+wush_status wush_quant(int fmt, const void* X, const void* T, int64_t M, int64_t K,
+                       const float* global_scale, void* codes, void* scales, uint32_t* n_exact,
+                       hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (fmt != wush::kMXFP4 && fmt != wush::kNVFP4 && fmt != wush::kINT4)
+    return fail(WUSH_EUNSUPPORTED, "unknown format %d", fmt);
+  const int G = (fmt == wush::kNVFP4) ? 16 : 32;
+  wush_status st = check_shape(X, T, M, K, G);
+  if (st != WUSH_OK || M == 0) return st;
+  if (!codes || !scales) return fail(WUSH_EINVAL, "null codes or scales");
+  if (fmt == wush::kNVFP4 && !global_scale) return fail(WUSH_EINVAL, "NVFP4 needs global_scale");
+  if (!aligned(codes, 8)) return fail(WUSH_EALIGN, "codes must be 8-byte aligned");
+  const int scale_bytes = (fmt == wush::kINT4) ? 2 : 1;
+  if (!aligned(scales, scale_bytes)) return fail(WUSH_EALIGN, "scales must be %d-byte aligned", scale_bytes);
+  if (global_scale && fmt == wush::kNVFP4 && !aligned(global_scale, 4))
+    return fail(WUSH_EALIGN, "global_scale must be 4-byte aligned");
+  if (n_exact && !aligned(n_exact, 4)) return fail(WUSH_EALIGN, "n_exact must be 4-byte aligned");
+  const uint64_t nx = (uint64_t)M * K * 2, nt = (uint64_t)K * G * 2;
+  const uint64_t nc = (uint64_t)M * K / 2, ns = (uint64_t)M * (K / G) * scale_bytes;
+  if (overlap(codes, nc, X, nx) || overlap(codes, nc, T, nt) || overlap(scales, ns, X, nx) ||
+      overlap(scales, ns, T, nt) || overlap(codes, nc, scales, ns))
+    return fail(WUSH_EINVAL, "output buffers overlap inputs or each other");
+  st = check_device();
+  if (st != WUSH_OK) return st;
+
+  wush::QuantArgs a{};
+  a.X = static_cast<const uint16_t*>(X);
+  a.T = static_cast<const uint16_t*>(T);
+  a.codes = static_cast<uint8_t*>(codes);
+  a.scales = static_cast<uint8_t*>(scales);
+  a.global_scale = global_scale;
+  a.n_exact = n_exact;
+  a.M = M;
+  a.K = K;
+  plan_quant(M, K, &a.n_tiles, &a.tiles_per_wave, &a.n_panels, &a.n_pg, &a.n_tg);
+  const int64_t n_wg = (int64_t)a.n_pg * a.n_tg;
+  if (n_wg > 0x7FFFFFFF) return fail(WUSH_EINVAL, "problem too large for one launch");
+  hipError_t e = wush::launch_quant(fmt, a, (int)n_wg, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+wush_status wush_quant_mxfp4(const void* X, const void* T, int64_t M, int64_t K, void* codes,
+                             void* scales, hipStream_t stream) {
+  return wush_quant(wush::kMXFP4, X, T, M, K, nullptr, codes, scales, nullptr, stream);
+}
+
+wush_status wush_quant_nvfp4(const void* X, const void* T, int64_t M, int64_t K,
+                             const float* global_scale, void* codes, void* scales,
+                             hipStream_t stream) {
+  return wush_quant(wush::kNVFP4, X, T, M, K, global_scale, codes, scales, nullptr, stream);
+}
+
+wush_status wush_quant_int4(const void* X, const void* T, int64_t M, int64_t K, void* codes,
+                            void* scales, hipStream_t stream) {
+  return wush_quant(wush::kINT4, X, T, M, K, nullptr, codes, scales, nullptr, stream);
+}
+
+static wush_status transform_common(const void* X, const void* T, int64_t M, int64_t K, int G,
+                                    float* Y, uint32_t* amax_bits, hipStream_t stream) {
+  wush::TransformArgs a{};
+  a.X = static_cast<const uint16_t*>(X);
+  a.T = static_cast<const uint16_t*>(T);
+  a.Y = Y;
+  a.amax_bits = amax_bits;
+  a.M = M;
+  a.K = K;
+  plan(M, K, &a.n_tiles, &a.tiles_per_wave, &a.n_panels, &a.n_pg, &a.n_tg);
+  const int64_t n_wg = (int64_t)a.n_pg * a.n_tg;
+  if (n_wg > 0x7FFFFFFF) return fail(WUSH_EINVAL, "problem too large for one launch");
+  hipError_t e = wush::launch_transform(G, amax_bits != nullptr, a, (int)n_wg, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+wush_status wush_transform_f32(const void* X, const void* T, int64_t M, int64_t K, int G, float* Y,
+                               hipStream_t stream) {
+  g_last_error[0] = 0;
+  wush_status st = check_shape(X, T, M, K, G);
+  if (st != WUSH_OK || M == 0) return st;
+  if (!Y) return fail(WUSH_EINVAL, "null Y");
+  if (!aligned(Y, 16)) return fail(WUSH_EALIGN, "Y must be 16-byte aligned");
+  if (overlap(Y, (uint64_t)M * K * 4, X, (uint64_t)M * K * 2) || overlap(Y, (uint64_t)M * K * 4, T, (uint64_t)K * G * 2))
+    return fail(WUSH_EINVAL, "Y overlaps an input");
+  st = check_device();
+  if (st != WUSH_OK) return st;
+  return transform_common(X, T, M, K, G, Y, nullptr, stream);
+}
+
+static wush_status absmax_common(const void* X, const void* T, int64_t M, int64_t K, int G, float* out,
+                                 hipStream_t stream) {
+  wush_status st = check_shape(X, T, M, K, G);
+  if (st != WUSH_OK) return st;
+  if (!out) return fail(WUSH_EINVAL, "null output");
+  if (!aligned(out, 4)) return fail(WUSH_EALIGN, "output must be 4-byte aligned");
+  if (M > 0 && (overlap(out, 4, X, (uint64_t)M * K * 2) || overlap(out, 4, T, (uint64_t)K * G * 2)))
+    return fail(WUSH_EINVAL, "output overlaps an input");
+  st = check_device();
+  if (st != WUSH_OK) return st;
+  if (M == 0) {
+    // The AbsMax of an empty tensor is 0.  Write it with the same fill
+    // kernel the non-empty path uses.
+    wush::TransformArgs a{};
+    a.amax_bits = reinterpret_cast<uint32_t*>(out);
+    a.K = K;
+    hipError_t e = wush::launch_transform(G, true, a, 0, stream);
+    (void)e;
+    return WUSH_OK;
+  }
+  return transform_common(X, T, M, K, G, nullptr, reinterpret_cast<uint32_t*>(out), stream);
+}
+
+wush_status wush_transformed_absmax(const void* X, const void* T, int64_t M, int64_t K, int G,
+                                    float* amax, hipStream_t stream) {
+  g_last_error[0] = 0;
+  return absmax_common(X, T, M, K, G, amax, stream);
+}
+
+wush_status wush_nvfp4_global_scale(const void* X, const void* T, int64_t M, int64_t K,
+                                    float* global_scale, hipStream_t stream) {
+  g_last_error[0] = 0;
+  wush_status st = absmax_common(X, T, M, K, 16, global_scale, stream);
+  if (st != WUSH_OK) return st;
+  hipError_t e = wush::launch_global_scale(global_scale, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+wush_status wush_e2m1_encode(const float* v, int64_t n, uint8_t* codes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (n < 0) return fail(WUSH_EINVAL, "n must be >= 0");
+  if (n == 0) return WUSH_OK;
+  if (!v || !codes) return fail(WUSH_EINVAL, "null pointer");
+  if (!aligned(v, 4)) return fail(WUSH_EALIGN, "v must be 4-byte aligned");
+  if (overlap(v, (uint64_t)n * 4, codes, (uint64_t)n)) return fail(WUSH_EINVAL, "codes overlaps v");
+  wush_status st = check_device();
+  if (st != WUSH_OK) return st;
+  hipError_t e = wush::launch_e2m1(v, n, codes, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,673 @@
+// Fused WUSH transform + 4-bit quantization kernels for gfx950 (CDNA4).
+//
+// The computation follows "WUSH: Near-Optimal Adaptive Transforms for LLM
+// Quantization".  Each G-channel block of a token row is multiplied by its
+// own T_wush(c) (Eq. 8), then RTN AbsMax-quantized in groups of G (deep
+// dive, sections 3.4.6 and 3.4.7; Eq. 10).  The pages' own kernel is a
+// CUTLASS GEMM in which each thread block takes one block index c.  This
+// design keeps only the idea that c is not a GEMM dimension.  The rest is
+// laid out for wave64 matrix cores:
+//
+//  * Tile.  One wave owns a panel of 32 channels (one G=32 block, or two
+//    G=16 blocks) for 32 tokens, and computes Y^T = T * X^T with two
+//    v_mfma_f32_32x32x16_bf16.  The A operand is T, loaded once per wave
+//    into VGPRs and reused across the wave's token tiles.  The B operand is
+//    X.  MFMA k-slice kk takes channels 16kk..16kk+15 of the panel, so each of
+//    the two 16-byte loads of a wave covers 32 contiguous bytes of 32 rows.
+//  * Output rows of T are permuted when the A fragment is loaded.  After the
+//    permutation, lane (n, h) holds outputs 16h..16h+15 of token n in
+//    accumulator registers 0..15.  A 32-group's AbsMax is then an in-lane max
+//    plus one exchange between lanes l and l^32.  A 16-group (NVFP4, with a
+//    block-diagonal pair as A) is entirely in-lane.
+//  * Exact scales.  A second MFMA pair computes A_i = sum_j |T_ij||x_j|,
+//    which bounds how far the fp32 accumulation can be from the exact sum.
+//    If a group's scale decision is not constant over
+//    [amax - d, amax + d], the wave recomputes that token's panel in
+//    float64.  The result is then the exactly rounded y.
+//
+// Memory layout and ABI: see include/wush.h.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wush_kernels.h"
+
+namespace wush {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWaves = kWavesPerGroup;  // waves per workgroup
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Output row held by A-operand row i, chosen so that D register r of lane
+// half h is output 16h + r.  The 32x32 D layout puts row
+// 8*(r/4) + 4*h + (r%4) in register r of half h.
+__device__ __forceinline__ int permuted_row(int i) {
+  return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+}
+
+// max(v[l], v[l ^ 32]) for non-negative v.  v_permlane32_swap returns v[l]
+// and v[l ^ 32] in its two results, in an order that depends on the lane
+// half.  Non-negative floats order like their bit patterns.
+__device__ __forceinline__ float max_halves(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0] > p[1] ? p[0] : p[1]);
+}
+
+// v[l] + v[l ^ 32], with the operands in the same order in both lanes of a
+// pair, so both get the same rounded sum.
+__device__ __forceinline__ double sum_halves(double v) {
+  uint64_t b = __builtin_bit_cast(uint64_t, v);
+  uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+  auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  double a = __builtin_bit_cast(double, ((uint64_t)ph[0] << 32) | pl[0]);
+  double c = __builtin_bit_cast(double, ((uint64_t)ph[1] << 32) | pl[1]);
+  return a + c;
+}
+
+__device__ __forceinline__ float max_abs16(const f32x16& v) {
+  float m = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(v[r]));
+  return m;
+}
+
+__device__ __forceinline__ float max16(const f32x16& v) {
+  float m = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m = fmaxf(m, v[r]);
+  return m;
+}
+
+// ---------------------------------------------------------------- codecs
+
+// E8M0 code of a non-negative finite amax: floor(log2 amax) - 2 + 127,
+// clamped below at 0 (e = -127).  amax < 2^128, so it never exceeds 252.
+__device__ __forceinline__ int e8m0_code(float amax) {
+  int be = (int)(__float_as_uint(amax) >> 23);
+  return be > 2 ? be - 2 : 0;
+}
+
+// E2M1 conversion of a pair: v_cvt_scalef32_pk_fp4_f32 divides both values
+// by 2^(exponent field of `scale`), rounds to nearest even, saturates at +-6,
+// keeps the sign of zero and writes a byte (first value in the low nibble)
+// into byte BYTE of `old`.  With scale = 1.0 it is plain E2M1 rounding.
+template <int BYTE>
+__device__ __forceinline__ uint32_t cvt_e2m1x2(uint32_t old, float a, float b, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, BYTE);
+}
+
+// OCP E4M3FN code of a non-negative finite x: nearest, ties to even, with
+// saturation at 448 (code 126).
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  if (x >= 448.0f) return 126u;
+  if (x < 0.015625f) {  // below 2^-6: subnormal grid, step 2^-9
+    return (uint32_t)__builtin_rintf(x * 512.0f);  // 0..8; 8 is 2^-6 = code 8
+  }
+  uint32_t b = __float_as_uint(x);
+  b = b + 0x7FFFFu + ((b >> 20) & 1u);  // round mantissa to 3 bits, ties to even
+  uint32_t c = (b >> 20) - (120u << 3);  // rebias exponent 127 -> 7
+  return c > 126u ? 126u : c;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  uint32_t e = c >> 3, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  _Float16 h = (_Float16)x;  // v_cvt_f16_f32: round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_value(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// ---------------------------------------------------------------- scale decisions
+//
+// Each decision is a monotone function of amax.  `unsure` reports whether it
+// could change anywhere in [amax - d, amax + d].
+
+__device__ __forceinline__ bool mx_unsure(float amax, float d) {
+  return e8m0_code(fmaxf(amax - d, 0.0f)) != e8m0_code(amax + d);
+}
+
+__device__ __forceinline__ bool int4_unsure(float amax, float d) {
+  float q = amax / 7.0f;
+  float dq = d * 0.15f + q * 0x1p-21f;
+  return f16_bits(fmaxf(q - dq, 0.0f)) != f16_bits(q + dq);
+}
+
+__device__ __forceinline__ bool nv_unsure(float amax, float d, float g) {
+  if (!(g > 0.0f)) return false;  // every code is zero whatever amax is
+  float ratio = (amax / 6.0f) / g;
+  if (amax == 0.0f) return d > 0.0f && e4m3_code((d / 6.0f) / g) != 0u;
+  // ratio scales linearly with amax; the relative slack covers roundings
+  float dr = ratio * (d * __builtin_amdgcn_rcpf(amax)) * 1.01f + ratio * 0x1p-20f;
+  return e4m3_code(fmaxf(ratio - dr, 0.0f)) != e4m3_code(ratio + dr);
+}
+
+// ---------------------------------------------------------------- fragments
+
+struct Frag {
+  u32x4 t0, t1;  // T rows (permuted), k-slices 0 and 1 of this lane half
+  u32x4 a0, a1;  // |T|
+};
+
+// Lane (i, h) of the A operand holds row permuted_row(i).  For k-slice kk
+// its 8 values are columns 16kk + 8h .. 16kk + 8h + 7 of the panel.
+// G == 32: panel p is block p.  G == 16: panel p is blocks 2p and 2p+1
+// placed block-diagonally, so output rows 16kk..16kk+15 see only block
+// 2p + kk through k-slice kk.
+template <int G>
+__device__ __forceinline__ Frag load_t(const uint16_t* __restrict__ T, int p, int C, int lane) {
+  Frag f;
+  const int i = lane & 31, h = lane >> 5;
+  const int row = permuted_row(i);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  f.t0 = z;
+  f.t1 = z;
+  if (G == 32) {
+    const uint16_t* src = T + ((size_t)p * 32 + row) * 32 + 8 * h;
+    f.t0 = *reinterpret_cast<const u32x4*>(src);
+    f.t1 = *reinterpret_cast<const u32x4*>(src + 16);
+  } else {
+    const int kk = row >> 4, blk = 2 * p + kk;
+    if (blk < C) {
+      u32x4 t = *reinterpret_cast<const u32x4*>(T + (size_t)blk * 256 + (row & 15) * 16 + 8 * h);
+      if (kk == 0) f.t0 = t;
+      else f.t1 = t;
+    }
+  }
+  f.a0 = z;  // |T| is filled in by with_abs() once the loads are in flight
+  f.a1 = z;
+  return f;
+}
+
+__device__ __forceinline__ void with_abs(Frag& f) {
+  const u32x4 mask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
+  f.a0 = f.t0 & mask;
+  f.a1 = f.t1 & mask;
+}
+
+struct XTile {
+  u32x4 b0, b1;
+};
+
+__device__ __forceinline__ u32x4 load16_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Recompute token `n`'s 32 outputs of the current panel in float64 and
+// write them into the accumulator of lanes (n, 0) and (n, 1).  Lane (i, h)
+// owns output row permuted_row(i).  It re-reads its half-row of T and forms
+// the half-h partial sum; lane l ^ 32 holds the other half.  The reads are
+// volatile, so the compiler cannot hoist this rare path's float64 copies of
+// T into registers that stay live across the hot loop.
+template <int G>
+__device__ __forceinline__ void exact_panel(int n, const uint16_t* T, int p, int C, const XTile& x, f32x16& acc,
+                                         float* lds, int lane) {
+  const int i = lane & 31, h = lane >> 5;
+  const int row = permuted_row(i);
+  u32x4 tk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  if (G == 32) {
+    const uint16_t* src = T + ((size_t)p * 32 + row) * 32 + 8 * h;
+    tk[0] = *reinterpret_cast<const volatile u32x4*>(src);
+    tk[1] = *reinterpret_cast<const volatile u32x4*>(src + 16);
+  } else {
+    const int kk = row >> 4, blk = 2 * p + kk;
+    if (blk < C) {
+      u32x4 t = *reinterpret_cast<const volatile u32x4*>(T + (size_t)blk * 256 + (row & 15) * 16 + 8 * h);
+      if (kk == 0) tk[0] = t;
+      else tk[1] = t;
+    }
+  }
+  const u32x4 bk[2] = {x.b0, x.b1};
+  double s = 0.0;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t x0 = __builtin_amdgcn_readlane(bk[kk][w], n);
+      uint32_t x1 = __builtin_amdgcn_readlane(bk[kk][w], n + 32);
+      uint32_t xw = h ? x1 : x0;
+      uint32_t tw = tk[kk][w];
+      s = __builtin_fma((double)bf16_lo(tw), (double)bf16_lo(xw), s);
+      s = __builtin_fma((double)bf16_hi(tw), (double)bf16_hi(xw), s);
+    }
+  }
+  const float y = (float)sum_halves(s);
+  if (h == 0) lds[row] = y;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (i == n) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = lds[16 * h + r];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 16 values -> 16 E2M1 codes in two words, value r in nibble r.  `scale` is
+// applied by the conversion as a division by 2^(its exponent field).
+__device__ __forceinline__ u32x2 pack_e2m1(const f32x16& v, float scale) {
+  uint32_t w0 = 0u, w1 = 0u;
+  w0 = cvt_e2m1x2<0>(w0, v[0], v[1], scale);
+  w0 = cvt_e2m1x2<1>(w0, v[2], v[3], scale);
+  w0 = cvt_e2m1x2<2>(w0, v[4], v[5], scale);
+  w0 = cvt_e2m1x2<3>(w0, v[6], v[7], scale);
+  w1 = cvt_e2m1x2<0>(w1, v[8], v[9], scale);
+  w1 = cvt_e2m1x2<1>(w1, v[10], v[11], scale);
+  w1 = cvt_e2m1x2<2>(w1, v[12], v[13], scale);
+  w1 = cvt_e2m1x2<3>(w1, v[14], v[15], scale);
+  u32x2 w = {w0, w1};
+  return w;
+}
+
+// INT4 element: rne(clamp(y * r, -7, 7)) as a two's-complement nibble.  After
+// adding 1.5 * 2^23, the low mantissa bits of the fp32 sum hold the rounded
+// integer.
+__device__ __forceinline__ uint32_t int4_bits(float y, float r) {
+  float v = fminf(fmaxf(y * r, -7.0f), 7.0f);
+  return __float_as_uint(v + 12582912.0f);
+}
+
+// Pack 16 INT4 values: v_perm_b32 gathers the low byte of four results into
+// one word (even elements in one word, odd in the other).  Then the two words
+// merge as nibble pairs.
+__device__ __forceinline__ uint32_t pack_int4x8(const f32x16& v, int base, float r) {
+  uint32_t q[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) q[k] = int4_bits(v[base + k], r);
+  // bytes {q0, q2, q4, q6} and {q1, q3, q5, q7}
+  uint32_t e01 = __builtin_amdgcn_perm(q[2], q[0], 0x0c0c0400u);  // [q0.b0, q2.b0, 0, 0]
+  uint32_t e23 = __builtin_amdgcn_perm(q[6], q[4], 0x04000c0cu);  // [0, 0, q4.b0, q6.b0]
+  uint32_t o01 = __builtin_amdgcn_perm(q[3], q[1], 0x0c0c0400u);
+  uint32_t o23 = __builtin_amdgcn_perm(q[7], q[5], 0x04000c0cu);
+  uint32_t ev = (e01 | e23) & 0x0F0F0F0Fu;
+  uint32_t od = (o01 | o23) & 0x0F0F0F0Fu;
+  return ev | (od << 4);
+}
+
+__device__ __forceinline__ u32x2 pack_int4(const f32x16& v, float r) {
+  u32x2 w = {pack_int4x8(v, 0, r), pack_int4x8(v, 8, r)};
+  return w;
+}
+
+// Bound on |fp32 MFMA result - exact sum| for a group whose |T||x| sums
+// peak at amax_abs.  The accumulation has at most 63 roundings of partial
+// sums bounded by amax_abs, each below 2^-23 relative (truncation is the
+// worst case), so 2^-17 covers it.  A term of 2^-21 * amax covers the final
+// rounding of y to fp32.  2^-120 covers products flushed at the bottom of
+// the fp32 range.
+__device__ __forceinline__ float err_bound(float amax_abs, float amax) {
+  return 0x1p-17f * amax_abs + 0x1p-21f * amax + 0x1p-120f;
+}
+
+// Workgroup -> (panel group, token group).  Workgroups are dispatched
+// round-robin over the 8 XCDs.  When the count divides evenly, each XCD
+// gets a contiguous range in panel-major order, so its L2 fetches each T
+// panel once.
+__device__ __forceinline__ void wg_coords(int n_pg, int n_tg, int& pg, int& tg) {
+  int b = blockIdx.x;
+  int n = n_pg * n_tg;
+  int logical = b;
+  if ((n & 7) == 0) logical = (b & 7) * (n >> 3) + (b >> 3);
+  pg = logical / n_tg;
+  tg = logical - pg * n_tg;
+}
+
+// Per-group scale and code computation for one panel of one 32-token tile.
+// Input: the panel's accumulators (lane (n, h) holds outputs 16h..16h+15 of
+// token n) and |T||x| sums.  Output: this lane's 16 codes (two words) and
+// its scale bits.  Groups whose scale decision is within the accumulation
+// bound of a boundary are recomputed exactly first.
+template <int FMT>
+__device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, const f32x16& aab, const uint16_t* T, int p,
+                                                int C, const XTile& x, float g, float* lds, int lane,
+                                                uint32_t& scale_bits, uint32_t& n_exact) {
+  constexpr int G = (FMT == kNVFP4) ? 16 : 32;
+  float amax = max_abs16(acc);
+  float aabs = max16(aab);
+  if (G == 32) {
+    amax = max_halves(amax);
+    aabs = max_halves(aabs);
+  }
+  const float d = err_bound(aabs, amax);
+  bool unsure;
+  if (FMT == kMXFP4) unsure = mx_unsure(amax, d);
+  else if (FMT == kINT4) unsure = int4_unsure(amax, d);
+  else unsure = nv_unsure(amax, d, g);
+  uint64_t pending = __ballot(unsure);
+  if (pending) {
+    while (pending) {
+      int ln = __builtin_ctzll(pending) & 31;
+      exact_panel<G>(ln, T, p, C, x, acc, lds, lane);
+      pending &= ~((1ull << ln) | (1ull << (ln + 32)));
+      n_exact += (lane == 0) ? 1u : 0u;
+    }
+    amax = max_abs16(acc);
+    if (G == 32) amax = max_halves(amax);
+  }
+  if (FMT == kMXFP4) {
+    uint32_t code = (uint32_t)e8m0_code(amax);
+    scale_bits = code;
+    // the E8M0 code is the biased exponent of 2^e: pass it as an fp32
+    return pack_e2m1(acc, __uint_as_float(code << 23));
+  } else if (FMT == kINT4) {
+    uint32_t sb = f16_bits(amax / 7.0f);
+    float s = f16_value(sb);
+    scale_bits = sb;
+    return pack_int4(acc, s > 0.0f ? 1.0f / s : 0.0f);
+  } else {
+    uint32_t code = 0;
+    float r = 0.0f;
+    if (g > 0.0f) {
+      code = e4m3_code((amax / 6.0f) / g);
+      float eff = e4m3_value(code) * g;
+      r = eff > 0.0f ? 1.0f / eff : 0.0f;
+    }
+    scale_bits = code;
+    f32x16 v;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = acc[k] * r;
+    return pack_e2m1(v, 1.0f);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- quant kernel
+//
+// Workgroup tile: 32 tokens x kPanels panels (256 channels).  Wave w owns
+// panels 2w and 2w+1 of the tile and keeps their T fragments in VGPRs for
+// all the tiles the workgroup walks.
+//
+// Per tile:
+//  1. The X tile (32 rows x 512 B) arrives through row-contiguous 16-byte
+//     loads: one wave instruction covers 2 rows x 512 B.  It is prefetched
+//     into registers one tile ahead, then written to LDS (rows padded to
+//     528 B, so the transposing reads below are bank-conflict free).
+//  2. Each wave reads its panels' MFMA B fragments from LDS, contracts,
+//     quantizes, and writes codes and scales into LDS output tiles.
+//  3. The output tiles leave as full rows: 32 rows x 128 B of codes (one
+//     16-byte store per thread) and 32 rows x 8..16 B of scales.
+// Rows past M are loaded from row M-1 and not stored.  Channels past K
+// (the last tile of a row) are not loaded; they are zero in LDS.
+
+constexpr int kPanels = 8;            // panels (32 channels each) per workgroup tile
+constexpr int kXRow = 512 + 16;       // LDS bytes per X row (256 bf16 + pad)
+constexpr int kCRow = 128 + 16;       // LDS bytes per code row (8 panels x 16 B + pad)
+constexpr int kSRow = 16;             // LDS bytes per scale row
+
+template <int FMT>
+__global__ __launch_bounds__(kWaves * 64) void quant_kernel(QuantArgs a) {
+  constexpr int G = (FMT == kNVFP4) ? 16 : 32;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[32 * kXRow];
+  __shared__ __attribute__((aligned(16))) uint8_t cs[32 * kCRow];
+  __shared__ __attribute__((aligned(16))) uint8_t ss[32 * kSRow];
+  __shared__ float lds_y[kWaves][32];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  int cg, tg;
+  wg_coords(a.n_pg, a.n_tg, cg, tg);
+  const int64_t K = a.K, M = a.M;
+  const int C = (int)(K / G);
+  const int p0 = cg * kPanels;  // first panel of the tile
+  const int n_panels = (a.n_panels - p0 < kPanels) ? a.n_panels - p0 : kPanels;
+
+  // T fragments of this wave's two panels (zero for panels past the end)
+  Frag f[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int pl = 2 * wave + j;
+    if (pl < n_panels) {
+      f[j] = load_t<G>(a.T, p0 + pl, C, lane);
+    } else {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      f[j] = Frag{z, z, z, z};
+    }
+  }
+
+  // Load mapping: instruction i (0..3) of thread t covers row 8i + t/32,
+  // 16-byte chunk t%32 of the 512-byte tile row.
+  const int chunk = tid & 31;
+  const int64_t ch0 = (int64_t)p0 * 32 + 8 * chunk;  // first channel of this thread's chunk
+  const bool chunk_ok = ch0 < K;
+  const int64_t tile0 = (int64_t)tg * a.tiles_per_wave;
+  const int64_t tile1 = (tile0 + a.tiles_per_wave < a.n_tiles) ? tile0 + a.tiles_per_wave : a.n_tiles;
+
+  u32x4 pre[4];
+  auto load_tile = [&](int64_t t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = t * 32 + 8 * i + (tid >> 5);
+      const int64_t mc = m < M ? m : M - 1;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      pre[i] = chunk_ok ? load16_nt(a.X + mc * K + ch0) : z;
+    }
+  };
+
+  float g = 0.0f;
+  if (FMT == kNVFP4) g = *a.global_scale;
+  uint32_t n_exact = 0;
+  const u32x4 mask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
+  const int n = lane & 31, h = lane >> 5;
+
+  // Valid bytes of a code row and of a scale row in this tile.
+  const int64_t code_bytes_left = K / 2 - (int64_t)p0 * 16;
+  const int code_row_bytes = (int)(code_bytes_left < kPanels * 16 ? code_bytes_left : kPanels * 16);
+  const int s_elem = (FMT == kINT4) ? 2 : 1;
+  const int64_t s_first = (G == 32) ? p0 : 2 * p0;  // first scale index of the tile in a row
+  const int s_count = (int)(((int64_t)C - s_first) < ((G == 32) ? kPanels : 2 * kPanels)
+                                ? (int64_t)C - s_first
+                                : ((G == 32) ? kPanels : 2 * kPanels));
+
+  if (tile0 < tile1) load_tile(tile0);
+  for (int64_t t = tile0; t < tile1; ++t) {
+    // 1. stage the tile in LDS, start loading the next one
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(xs + (8 * i + (tid >> 5)) * kXRow + 16 * chunk) = pre[i];
+    if (t + 1 < tile1) load_tile(t + 1);
+    __syncthreads();
+
+    // 2. contract and quantize this wave's panels
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pl = 2 * wave + j;
+      if (pl >= n_panels) break;
+      XTile x;
+      const uint8_t* row = xs + n * kXRow + pl * 64 + 16 * h;
+      x.b0 = *reinterpret_cast<const u32x4*>(row);
+      x.b1 = *reinterpret_cast<const u32x4*>(row + 32);
+      f32x16 zero = {};
+      f32x16 acc = mfma32(f[j].t0, x.b0, zero);
+      acc = mfma32(f[j].t1, x.b1, acc);
+      f32x16 aab = mfma32(f[j].t0 & mask, x.b0 & mask, zero);
+      aab = mfma32(f[j].t1 & mask, x.b1 & mask, aab);
+      uint32_t sbits;
+      const u32x2 w = quantize_panel<FMT>(acc, aab, a.T, p0 + pl, C, x, g, lds_y[wave], lane, sbits, n_exact);
+      *reinterpret_cast<u32x2*>(cs + n * kCRow + pl * 16 + 8 * h) = w;
+      if (FMT == kMXFP4) {
+        if (h == 0) ss[n * kSRow + pl] = (uint8_t)sbits;
+      } else if (FMT == kINT4) {
+        if (h == 0) *reinterpret_cast<uint16_t*>(ss + n * kSRow + 2 * pl) = (uint16_t)sbits;
+      } else {
+        ss[n * kSRow + 2 * pl + h] = (uint8_t)sbits;
+      }
+    }
+    __syncthreads();
+
+    // 3. write the tile's codes and scales as whole rows
+    {
+      const int r = tid >> 3, jc = tid & 7;  // row, 16-byte chunk
+      const int64_t m = t * 32 + r;
+      if (m < M && 16 * jc < code_row_bytes) {
+        uint8_t* dst = a.codes + m * (K / 2) + (int64_t)p0 * 16 + 16 * jc;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(cs + r * kCRow + 16 * jc);
+        if (16 * jc + 16 <= code_row_bytes) {
+          *reinterpret_cast<u32x4*>(dst) = v;
+        } else {  // a G=16 row ending half-way into the last panel
+          u32x2 h8 = {v[0], v[1]};
+          *reinterpret_cast<u32x2*>(dst) = h8;
+        }
+      }
+    }
+    if (tid < 32) {
+      const int64_t m = t * 32 + tid;
+      if (m < M) {
+        uint8_t* dst = a.scales + (m * C + s_first) * s_elem;
+        const uint8_t* src = ss + tid * kSRow;
+        const int nb = s_count * s_elem;
+        if (nb == 8 && ((uintptr_t)dst & 7) == 0) {
+          *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const u32x2*>(src);
+        } else if (nb == 16 && ((uintptr_t)dst & 15) == 0) {
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          for (int b = 0; b < nb; ++b) dst[b] = src[b];
+        }
+      }
+    }
+    // the next iteration overwrites xs only after this barrier-free store
+    // phase; the barrier after its LDS writes orders the cs/ss reuse.
+    __syncthreads();
+  }
+  if (a.n_exact && n_exact) atomicAdd(a.n_exact, n_exact);
+}
+
+// ---------------------------------------------------------------- transform / absmax
+
+template <int G, bool ABSMAX>
+__global__ __launch_bounds__(kWaves * 64) void transform_kernel(TransformArgs a) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  int pg, tg;
+  wg_coords(a.n_pg, a.n_tg, pg, tg);
+  const int p = pg * kWaves + wave;
+  if (p >= a.n_panels) return;
+  const int n = lane & 31, h = lane >> 5;
+  const int C = (int)(a.K / G);
+  const Frag f = load_t<G>(a.T, p, C, lane);
+  const int c_in = 32 * p + 8 * h;
+  const int d1 = ((G == 32) || (2 * p + 1 < C)) ? 16 : 0;
+  const int out0 = 32 * p + 16 * h;  // first output channel held by this lane
+  const bool group_ok = (G == 32) || (2 * p + h < C);
+  const int64_t tile0 = (int64_t)tg * a.tiles_per_wave;
+  const int64_t tile1 = (tile0 + a.tiles_per_wave < a.n_tiles) ? tile0 + a.tiles_per_wave : a.n_tiles;
+  float wmax = 0.0f;
+  for (int64_t t = tile0; t < tile1; ++t) {
+    const int64_t m = t * 32 + n;
+    const uint16_t* src = a.X + (m < a.M ? m : a.M - 1) * a.K + c_in;
+    XTile x;
+    x.b0 = load16_nt(src);
+    x.b1 = load16_nt(src + d1);
+    f32x16 zero = {};
+    f32x16 acc = mfma32(f.t0, x.b0, zero);
+    acc = mfma32(f.t1, x.b1, acc);
+    if (m >= a.M) continue;
+    if (ABSMAX) {
+      if (group_ok) wmax = fmaxf(wmax, max_abs16(acc));
+    } else if (group_ok) {
+      f32x4* dst = reinterpret_cast<f32x4*>(a.Y + m * a.K + out0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        __builtin_nontemporal_store(v, &dst[q]);
+      }
+    }
+  }
+  if (ABSMAX) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) wmax = fmaxf(wmax, __shfl_xor(wmax, o, 64));
+    if (lane == 0) atomicMax(a.amax_bits, __float_as_uint(wmax));  // non-negative floats order as uints
+  }
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v) { *p = v; }
+
+__global__ void global_scale_kernel(float* out) {
+  // out holds the AbsMax bit pattern written by the absmax kernel
+  float amax = __uint_as_float(*reinterpret_cast<uint32_t*>(out));
+  *out = amax / 2688.0f;
+}
+
+// Element i is converted as part of the pair (2*(i/2), 2*(i/2)+1), exactly as
+// the quantization kernels convert pairs, and written back one code per byte.
+__global__ void e2m1_kernel(const float* __restrict__ v, int64_t n, uint8_t* __restrict__ out) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; 2 * i < n; i += stride) {
+    float a = v[2 * i];
+    float b = (2 * i + 1 < n) ? v[2 * i + 1] : 0.0f;
+    uint32_t w = cvt_e2m1x2<0>(0u, a, b, 1.0f);
+    out[2 * i] = (uint8_t)(w & 0xFu);
+    if (2 * i + 1 < n) out[2 * i + 1] = (uint8_t)((w >> 4) & 0xFu);
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int FMT>
+static hipError_t launch_quant_fmt(const QuantArgs& a, int n_wg, hipStream_t s) {
+  hipLaunchKernelGGL((quant_kernel<FMT>), dim3(n_wg), dim3(kWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant(int fmt, const QuantArgs& a, int n_wg, hipStream_t s) {
+  switch (fmt) {
+    case kMXFP4: return launch_quant_fmt<kMXFP4>(a, n_wg, s);
+    case kNVFP4: return launch_quant_fmt<kNVFP4>(a, n_wg, s);
+    case kINT4: return launch_quant_fmt<kINT4>(a, n_wg, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_transform(int G, bool absmax, const TransformArgs& a, int n_wg, hipStream_t s) {
+  dim3 grid(n_wg), block(kWaves * 64);
+  if (absmax) {
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(1), 0, s, a.amax_bits, 0u);
+    if (n_wg == 0) return hipGetLastError();
+    if (G == 32) hipLaunchKernelGGL((transform_kernel<32, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((transform_kernel<16, true>), grid, block, 0, s, a);
+  } else {
+    if (G == 32) hipLaunchKernelGGL((transform_kernel<32, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((transform_kernel<16, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_global_scale(float* out, hipStream_t s) {
+  hipLaunchKernelGGL(global_scale_kernel, dim3(1), dim3(1), 0, s, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_e2m1(const float* v, int64_t n, uint8_t* out, hipStream_t s) {
+  int64_t blocks = (n / 2 + 256) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(e2m1_kernel, dim3((unsigned)blocks), dim3(256), 0, s, v, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace wush

@@ -1,0 +1,121 @@
+"""PyTorch-facing wrappers over the C ABI (argument marshalling only).
+
+Every function takes device tensors on the current HIP device.  It allocates
+the outputs with torch unless the caller passes them, and enqueues the
+library call on torch's current stream.  No arithmetic of the path runs here.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_G = {"mxfp4": 32, "nvfp4": 16, "int4": 32}
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check_x_t(X: torch.Tensor, T: torch.Tensor, G: int) -> Tuple[int, int]:
+    if X.dtype != torch.bfloat16 or T.dtype != torch.bfloat16:
+        raise TypeError("X and T must be bfloat16")
+    if not (X.is_cuda and T.is_cuda):
+        raise ValueError("X and T must be device tensors")
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    M, K = X.shape
+    if T.dim() != 3 or tuple(T.shape[1:]) != (G, G) or T.shape[0] * G != K:
+        raise ValueError("T must be [K/%d, %d, %d] for K=%d, got %s" % (G, G, G, K, tuple(T.shape)))
+    if not (X.is_contiguous() and T.is_contiguous()):
+        raise ValueError("X and T must be contiguous")
+    return M, K
+
+
+def quant(fmt: str, X: torch.Tensor, T: torch.Tensor, global_scale: Optional[torch.Tensor] = None,
+          codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+          n_exact: Optional[torch.Tensor] = None):
+    """Fused transform + quantization.  Returns (codes, scales)."""
+    G = _G[fmt]
+    M, K = _check_x_t(X, T, G)
+    dev = X.device
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        sdt = torch.float16 if fmt == "int4" else torch.uint8
+        scales = torch.empty((M, K // G), dtype=sdt, device=dev)
+    for t, shape in ((codes, (M, K // 2)), (scales, (M, K // G))):
+        if tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
+            raise ValueError("output buffer has the wrong shape, layout or device")
+    gs = 0
+    if fmt == "nvfp4":
+        if global_scale is None or global_scale.dtype != torch.float32 or global_scale.numel() != 1:
+            raise ValueError("nvfp4 needs a 1-element float32 global_scale tensor")
+        gs = global_scale.data_ptr()
+    ne = 0
+    if n_exact is not None:
+        if n_exact.dtype != torch.int32 or n_exact.numel() != 1:
+            raise ValueError("n_exact must be a 1-element int32 tensor")
+        ne = n_exact.data_ptr()
+    lib = _lib.load()
+    st = lib.wush_quant(_lib.FMT[fmt], X.data_ptr(), T.data_ptr(), M, K, gs or None, codes.data_ptr(),
+                        scales.data_ptr(), ne or None, _stream())
+    _lib.check(st, "wush_quant(%s)" % fmt)
+    return codes, scales
+
+
+def quant_mxfp4(X, T, codes=None, scales=None):
+    return quant("mxfp4", X, T, codes=codes, scales=scales)
+
+
+def quant_nvfp4(X, T, global_scale, codes=None, scales=None):
+    return quant("nvfp4", X, T, global_scale=global_scale, codes=codes, scales=scales)
+
+
+def quant_int4(X, T, codes=None, scales=None):
+    return quant("int4", X, T, codes=codes, scales=scales)
+
+
+def transform_f32(X: torch.Tensor, T: torch.Tensor, Y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    G = T.shape[-1]
+    M, K = _check_x_t(X, T, G)
+    if Y is None:
+        Y = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    lib = _lib.load()
+    _lib.check(lib.wush_transform_f32(X.data_ptr(), T.data_ptr(), M, K, G, Y.data_ptr(), _stream()),
+               "wush_transform_f32")
+    return Y
+
+
+def transformed_absmax(X: torch.Tensor, T: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    G = T.shape[-1]
+    M, K = _check_x_t(X, T, G)
+    if out is None:
+        out = torch.empty((1,), dtype=torch.float32, device=X.device)
+    lib = _lib.load()
+    _lib.check(lib.wush_transformed_absmax(X.data_ptr(), T.data_ptr(), M, K, G, out.data_ptr(), _stream()),
+               "wush_transformed_absmax")
+    return out
+
+
+def nvfp4_global_scale(X: torch.Tensor, T: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    M, K = _check_x_t(X, T, 16)
+    if out is None:
+        out = torch.empty((1,), dtype=torch.float32, device=X.device)
+    lib = _lib.load()
+    _lib.check(lib.wush_nvfp4_global_scale(X.data_ptr(), T.data_ptr(), M, K, out.data_ptr(), _stream()),
+               "wush_nvfp4_global_scale")
+    return out
+
+
+def e2m1_encode(v: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if v.dtype != torch.float32 or not v.is_cuda or not v.is_contiguous():
+        raise ValueError("v must be a contiguous float32 device tensor")
+    if out is None:
+        out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    lib = _lib.load()
+    _lib.check(lib.wush_e2m1_encode(v.data_ptr(), v.numel(), out.data_ptr(), _stream()), "wush_e2m1_encode")
+    return out

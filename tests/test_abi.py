@@ -1,0 +1,79 @@
+"""C-ABI checks that need no GPU.  The library loads, it exports every
+symbol include/wush.h declares, and argument validation rejects bad calls
+before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_activation_amd as wush
+from mxfp4_activation_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "wush.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wush_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = wush.load()
+    decl = _declared_symbols()
+    assert len(decl) >= 10
+    for name in decl:
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, "binding lacks " + name
+    assert set(_lib.SIGNATURES) == set(decl)
+    assert lib.wush_abi_version() == 1
+
+
+def test_status_strings():
+    lib = wush.load()
+    for s in range(5):
+        assert lib.wush_status_string(s)
+
+
+A = 1 << 20  # a 16-byte-aligned fake device address; validation never dereferences it
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_validation_rejects_bad_arguments(fmt):
+    lib = wush.load()
+    G = 16 if fmt == 1 else 32
+    gs = 3 << 20
+    q = lambda X, T, M, K, c, s, g=gs: lib.wush_quant(fmt, X, T, M, K, g, c, s, None, None)
+    assert q(A, A * 2, 0, 4 * G, None, None) == _lib.WUSH_OK  # empty batch: no-op
+    assert q(A, A * 2, -1, 4 * G, A * 3, A * 4) == _lib.WUSH_EINVAL
+    assert q(A, A * 2, 8, G + 1, A * 3, A * 4) == _lib.WUSH_EINVAL
+    assert q(A, A * 2, 8, 0, A * 3, A * 4) == _lib.WUSH_EINVAL
+    assert q(None, A * 2, 8, G, A * 3, A * 4) == _lib.WUSH_EINVAL
+    assert q(A, A * 2, 8, G, None, A * 4) == _lib.WUSH_EINVAL
+    assert q(A + 2, A * 2, 8, G, A * 3, A * 4) == _lib.WUSH_EALIGN
+    assert q(A, A * 2 + 8, 8, G, A * 3, A * 4) == _lib.WUSH_EALIGN
+    assert q(A, A * 2, 8, G, A * 3 + 4, A * 4) == _lib.WUSH_EALIGN
+    # codes overlapping X
+    assert q(A, A * 8, 8, 4 * G, A + 64, A * 16) == _lib.WUSH_EINVAL
+    if fmt == 1:
+        assert q(A, A * 2, 8, G, A * 3, A * 4, None) == _lib.WUSH_EINVAL
+    if fmt == 2:
+        assert q(A, A * 2, 8, G, A * 3, A * 4 + 1) == _lib.WUSH_EALIGN
+    assert lib.wush_last_error()
+
+
+def test_unknown_format_and_G():
+    lib = wush.load()
+    assert lib.wush_quant(7, A, A, 8, 32, None, A, A, None, None) == _lib.WUSH_EUNSUPPORTED
+    assert lib.wush_transform_f32(A, A * 2, 8, 64, 8, A * 4, None) == _lib.WUSH_EUNSUPPORTED
+    assert lib.wush_e2m1_encode(A, -1, A * 2, None) == _lib.WUSH_EINVAL
+    assert lib.wush_e2m1_encode(A, 0, None, None) == _lib.WUSH_OK
+
+
+def test_binding_raises_with_detail():
+    lib = wush.load()
+    st = lib.wush_quant_mxfp4(A, A, 8, 33, A * 2, A * 3, None)
+    with pytest.raises(_lib.WushError, match="multiple of 32"):
+        _lib.check(st, "wush_quant_mxfp4")

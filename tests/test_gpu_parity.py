@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every test here runs the kernels on the current HIP device and compares them,
+element by element, with ``oracle``.  The oracle gets the same seeded bf16
+inputs.  The bar is in tests/parity.py.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import codecs, quant
+from oracle import transform as tr
+from synthetic import CONFIGS, f64_to_bf16_bits
+
+from . import cases, parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import mxfp4_activation_amd as wush
+
+    wush.load()  # raises if libwush.so is missing: no fallback
+    yield
+
+
+def _dev_bf16(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _run(fmt, x_bits, t_bits, g=None, n_exact=False):
+    from mxfp4_activation_amd import ops
+
+    X, T = _dev_bf16(x_bits), _dev_bf16(t_bits)
+    gs = None
+    if fmt == "nvfp4":
+        gs = torch.tensor([np.float32(g)], dtype=torch.float32, device="cuda")
+    ne = torch.zeros(1, dtype=torch.int32, device="cuda") if n_exact else None
+    codes, scales = ops.quant(fmt, X, T, global_scale=gs, n_exact=ne)
+    torch.cuda.synchronize()
+    c = codes.cpu().numpy()
+    s = scales.cpu().numpy()
+    if fmt == "int4":
+        s = s.view(np.uint16)
+    if n_exact:
+        return c, s, int(ne.item())
+    return c, s
+
+
+def _g_for(x_bits, t_bits):
+    return quant.nvfp4_global_scale(quant.tensor_amax_ref(quant.transform_ref(x_bits, t_bits)))
+
+
+# ---------------------------------------------------------------- element codec
+
+
+def test_e2m1_encode_matches_oracle_on_fp32_octaves():
+    """Every fp32 pattern with |v| in [2^-3, 8), both signs, plus values above
+    and below that range and the exact ties."""
+    from mxfp4_activation_amd import ops
+
+    mant = np.arange(1 << 23, dtype=np.uint32)
+    for exp in range(-3, 3):
+        pos = (np.uint32((exp + 127) << 23) | mant).view(np.float32)
+        for v in (pos, -pos):
+            got = ops.e2m1_encode(torch.from_numpy(v).cuda()).cpu().numpy()
+            np.testing.assert_array_equal(got, codecs.e2m1_encode(v), err_msg="octave 2^%d" % exp)
+    rng = np.random.default_rng(0)
+    extra = np.concatenate([
+        rng.uniform(0, 0.125, 100000), np.exp(rng.uniform(np.log(8), np.log(3e38), 100000)),
+        [0.0, -0.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 8.0, 1e-45]]).astype(np.float32)
+    for v in (extra, -extra):
+        got = ops.e2m1_encode(torch.from_numpy(v).cuda()).cpu().numpy()
+        np.testing.assert_array_equal(got, codecs.e2m1_encode(v))
+
+
+# ---------------------------------------------------------------- tiny workload
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_tiny_workload(fmt):
+    G = 16 if fmt == "nvfp4" else 32
+    _, tb = cases.transforms("tiny_mxfp4", G)
+    xb = cases.x_full("tiny_mxfp4")
+    g = _g_for(xb, tb) if fmt == "nvfp4" else None
+    c, s = _run(fmt, xb, tb, g)
+    rep = parity.check(fmt, xb, tb, c, s, g)
+    print(fmt, rep)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+@pytest.mark.parametrize("M,K", [(1, 32), (31, 64), (33, 256), (100, 96), (257, 160), (64, 48)])
+def test_ragged_shapes(fmt, M, K):
+    G = 16 if fmt == "nvfp4" else 32
+    if K % G:
+        pytest.skip("K not a multiple of G")
+    if fmt != "nvfp4" and K % 32:
+        pytest.skip("K must be a multiple of 32")
+    rng = np.random.default_rng(M * 1000 + K)
+    X = rng.standard_t(3, (M, K))
+    X[:, rng.choice(K, max(1, K // 64), replace=False)] *= 30
+    W = rng.standard_normal((2 * K, K)) * 0.02
+    Xc = rng.standard_t(3, (4 * K, K))
+    T64, _ = tr.build_transforms(W, Xc, G)
+    xb, tb = f64_to_bf16_bits(X), tr.transforms_to_bf16_bits(T64)
+    g = _g_for(xb, tb) if fmt == "nvfp4" else None
+    c, s = _run(fmt, xb, tb, g)
+    parity.check(fmt, xb, tb, c, s, g)
+
+
+def test_empty_batch_is_noop():
+    import mxfp4_activation_amd as wush
+
+    lib = wush.load()
+    assert lib.wush_quant_mxfp4(None, None, 0, 256, None, None, None) == 0
+    X = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    T = torch.zeros((2, 32, 32), dtype=torch.bfloat16, device="cuda")
+    c, s = wush.quant_mxfp4(X, T)
+    assert c.shape == (0, 32) and s.shape == (0, 2)
+
+
+# ---------------------------------------------------------------- special transforms
+
+
+@pytest.mark.parametrize("which", ["identity", "hadamard", "cyclic"])
+def test_special_transforms(which):
+    wl = CONFIGS["tiny_mxfp4"]
+    G, C = 32, wl.C
+    if which == "identity":
+        T = np.broadcast_to(np.eye(G), (C, G, G))
+    elif which == "hadamard":
+        T = np.broadcast_to(tr.hadamard(G), (C, G, G))
+    else:
+        T = np.zeros((C, G, G))
+        for c in range(C):
+            for k in range(G):
+                T[c, k, (k + 2 * c + 1) % G] = 1.0
+    tb = f64_to_bf16_bits(np.ascontiguousarray(T))
+    xb = cases.x_full("tiny_mxfp4")
+    for fmt in ("mxfp4", "int4"):
+        c, s = _run(fmt, xb, tb)
+        parity.check(fmt, xb, tb, c, s)
+
+
+def test_scale_boundaries_take_exact_path():
+    """Groups whose maximum is an exact power of two sit on an E8M0 boundary.
+    The kernel must detect them and recompute them exactly, so the scale
+    stays bit-exact."""
+    G, M = 32, 64
+    rng = np.random.default_rng(5)
+    X = rng.uniform(-1, 1, (M, 4 * G))
+    X[:, ::G] = 2.0 ** rng.integers(-8, 8, (M, 4))  # an exact power of two in every group
+    xb = f64_to_bf16_bits(X)
+    tb = f64_to_bf16_bits(np.broadcast_to(np.eye(G), (4, G, G)).copy())
+    c, s, n = _run("mxfp4", xb, tb, n_exact=True)
+    parity.check("mxfp4", xb, tb, c, s)
+    assert n >= 1
+    c, s, n = _run("int4", xb, tb, n_exact=True)
+    parity.check("int4", xb, tb, c, s)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_extreme_magnitudes(fmt):
+    """Groups of tiny values (bf16 subnormals, E8M0 code 0), huge values (fp16
+    scale overflow for INT4), all-zero groups, and a mix, through T = I and
+    a random T."""
+    G = 16 if fmt == "nvfp4" else 32
+    rng = np.random.default_rng(11)
+    C, M = 8, 96
+    X = rng.standard_normal((M, C * G))
+    X[0:8] *= 2.0 ** -128  # subnormal region
+    X[8:16] *= 2.0 ** -122
+    X[16:24] *= 2.0 ** 100
+    X[24:32] = 0.0
+    X[32:40, ::2] *= 2.0 ** -60  # wide spread inside a group
+    X[40:48] *= 2.0 ** 18  # INT4 scale beyond fp16 range
+    xb = f64_to_bf16_bits(X)
+    for T in (np.broadcast_to(np.eye(G), (C, G, G)), rng.standard_normal((C, G, G)) * 0.3):
+        tb = f64_to_bf16_bits(np.ascontiguousarray(T))
+        g = _g_for(xb, tb) if fmt == "nvfp4" else None
+        c, s = _run(fmt, xb, tb, g)
+        parity.check(fmt, xb, tb, c, s, g)
+
+
+# ---------------------------------------------------------------- full sizes (sampled rows)
+
+
+@pytest.mark.parametrize("name", ["llama8b_mxfp4", "downproj_mxfp4", "nvfp4", "int4"])
+def test_full_size_sampled_rows(name):
+    wl = CONFIGS[name]
+    print("case", name, wl.M, wl.K, flush=True)
+    _, tb = cases.transforms(name)
+    xb = cases.x_full(name)
+    rows = cases.sample_rows(wl.M)
+    g = cases.oracle_global_scale(name) if wl.fmt == "nvfp4" else None
+    c, s, n = _run(wl.fmt, xb, tb, g, n_exact=True)
+    rep = parity.check(wl.fmt, xb[rows], tb, c[rows], s[rows], g)
+    print(name, rep, "exact groups:", n, "of", wl.M * wl.C, flush=True)
+
+
+# ---------------------------------------------------------------- support entry points
+
+
+@pytest.mark.parametrize("G", [16, 32])
+def test_transform_f32_error_bounds(G):
+    _, tb = cases.transforms("tiny_mxfp4", G)
+    T64, _ = cases.transforms("tiny_mxfp4", G)
+    xb = cases.x_full("tiny_mxfp4")
+    from mxfp4_activation_amd import ops
+
+    Y = ops.transform_f32(_dev_bf16(xb), _dev_bf16(tb)).cpu().numpy()
+    y_ref, A = quant.transform_ref(xb, tb, return_abs=True)
+    # the accumulation bound assumed by the scale fix-up
+    bound = (2.0 ** -17) * A + (2.0 ** -21) * np.abs(y_ref) + 2.0 ** -120
+    assert np.all(np.abs(Y.astype(np.float64) - y_ref) <= bound)
+    # Pre-quantization tolerance: within 2e-3 of the group AbsMax of the
+    # oracle's values for the same bf16 T.
+    M, K = y_ref.shape
+    err = np.abs(Y - y_ref).reshape(M, K // G, G).max(axis=2)
+    amax = np.abs(y_ref).reshape(M, K // G, G).max(axis=2)
+    assert np.all(err <= 2e-3 * amax)
+    # Against the unrounded float64 T, the extra error is bf16 storage of T.
+    # Each entry moves by at most bf16's unit roundoff 2^-8 relative, plus
+    # 2^-24 from the fp32 step.  So |y - y64| <= (2^-8 + 2^-23) *
+    # sum_j |T64_kj x_j| plus the bound above.
+    y64 = quant.transform_f64(xb, T64)
+    X = codecs.bf16_bits_to_f32(xb).astype(np.float64).reshape(M, K // G, G)
+    A64 = np.einsum("mcj,ckj->mck", np.abs(X), np.abs(T64)).reshape(M, K)
+    assert np.all(np.abs(Y - y64) <= (2.0 ** -8 + 2.0 ** -23) * A64 + bound)
+    rel = (np.abs(Y - y64).reshape(M, K // G, G).max(axis=2) / np.abs(y64).reshape(M, K // G, G).max(axis=2))
+    print("G=%d relative error vs float64 T: median %.2e, max %.2e" % (G, np.median(rel), rel.max()))
+
+
+def test_absmax_and_global_scale():
+    from mxfp4_activation_amd import ops
+
+    _, tb = cases.transforms("tiny_mxfp4", 16)
+    xb = cases.x_full("tiny_mxfp4")
+    y, A = quant.transform_ref(xb, tb, return_abs=True)
+    X, T = _dev_bf16(xb), _dev_bf16(tb)
+    amax = float(ops.transformed_absmax(X, T).item())
+    ref = float(quant.tensor_amax_ref(y))
+    assert abs(amax - ref) <= (2.0 ** -17) * A.max() + (2.0 ** -21) * ref
+    g = float(ops.nvfp4_global_scale(X, T).item())
+    assert g == float(np.float32(np.float32(amax) / np.float32(2688.0)))
+
+
+def test_deterministic_and_in_bounds():
+    """Two runs give identical bytes.  Canary bytes around the outputs stay
+    untouched."""
+    from mxfp4_activation_amd import ops
+
+    _, tb = cases.transforms("tiny_mxfp4")
+    xb = cases.x_full("tiny_mxfp4")
+    M, K = xb.shape
+    X, T = _dev_bf16(xb), _dev_bf16(tb)
+    pad = 4096
+    cbuf = torch.full((pad + M * K // 2 + pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((pad + M * K // 32 + pad,), 0x5A, dtype=torch.uint8, device="cuda")
+    codes = cbuf[pad:pad + M * K // 2].view(M, K // 2)
+    scales = sbuf[pad:pad + M * K // 32].view(M, K // 32)
+    ops.quant("mxfp4", X, T, codes=codes, scales=scales)
+    first = (codes.clone(), scales.clone())
+    ops.quant("mxfp4", X, T, codes=codes, scales=scales)
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], codes) and torch.equal(first[1], scales)
+    cb, sb = cbuf.cpu().numpy(), sbuf.cpu().numpy()
+    assert np.all(cb[:pad] == 0xA5) and np.all(cb[-pad:] == 0xA5)
+    assert np.all(sb[:pad] == 0x5A) and np.all(sb[-pad:] == 0x5A)
