@@ -84,24 +84,24 @@ void plan(int64_t M, int64_t K, int64_t* n_tiles, int64_t* tpw, int* n_panels, i
   *n_tg = (int)((*n_tiles + t - 1) / t);
 }
 
-// Quant kernel split: a workgroup owns a 32-token x 256-channel tile
-// column (kPanelsPerTile panels) and walks a run of 32-token tiles down it.
-// Runs are as long as possible while the grid still gives every CU about
-// 4 workgroups (256 CUs).  Longer runs amortize the T fragment loads and
-// let the next tile's loads overlap the current tile's compute.
-// WUSH_TILES_PER_WG overrides the run length (1..64) for tuning.
+// Quant kernel split: a workgroup (8 waves) owns a 256-channel column of
+// the input and walks a run of TPW 32-token tiles down it, with all of the
+// run's loads issued at entry.  TPW (1, 2, 4 or 8) is the longest run that
+// still gives at least 512 workgroups (two per CU, all resident at once), so
+// short batches still spread over every CU.  WUSH_TILES_PER_WG overrides
+// it for tuning.
 void plan_quant(int64_t M, int64_t K, int64_t* n_tiles, int64_t* tpw, int* n_panels, int* n_pg, int* n_tg) {
   *n_tiles = (M + 31) / 32;
   *n_panels = (int)((K + 31) / 32);
   *n_pg = (*n_panels + wush::kPanelsPerTile - 1) / wush::kPanelsPerTile;
-  const int64_t target_wg = 1024;
-  int64_t t = 16;
+  const int64_t target_wg = 512;
+  int64_t t = 8;
   while (t > 1 && (int64_t)(*n_pg) * ((*n_tiles + t - 1) / t) < target_wg) t >>= 1;
   static const int64_t env = [] {
     const char* s = getenv("WUSH_TILES_PER_WG");
     return s ? (int64_t)atoll(s) : (int64_t)0;
   }();
-  if (env >= 1 && env <= 64) t = env;
+  if (env == 1 || env == 2 || env == 4 || env == 8) t = env;
   *tpw = t;
   *n_tg = (int)((*n_tiles + t - 1) / t);
 }

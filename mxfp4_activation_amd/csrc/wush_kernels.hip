@@ -320,7 +320,7 @@ __device__ __forceinline__ u32x2 pack_int4(const f32x16& v, float r) {
 // rounding of y to fp32.  2^-120 covers products flushed at the bottom of
 // the fp32 range.
 __device__ __forceinline__ float err_bound(float amax_abs, float amax) {
-  return 0x1p-17f * amax_abs + 0x1p-21f * amax + 0x1p-120f;
+  return __builtin_fmaf(0x1p-17f, amax_abs, __builtin_fmaf(0x1p-21f, amax, 0x1p-120f));
 }
 
 // Workgroup -> (panel group, token group).  Workgroups are dispatched
@@ -338,25 +338,28 @@ __device__ __forceinline__ void wg_coords(int n_pg, int n_tg, int& pg, int& tg) 
 
 // Per-group scale and code computation for one panel of one 32-token tile.
 // Input: the panel's accumulators (lane (n, h) holds outputs 16h..16h+15 of
-// token n) and |T||x| sums.  Output: this lane's 16 codes (two words) and
-// its scale bits.  Groups whose scale decision is within the accumulation
-// bound of a boundary are recomputed exactly first.
+// token n) and `bound`, an upper bound on sum_j |T_kj x_j| over the lane's
+// group.  Output: this lane's 16 codes (two words) and its scale bits.
+// Groups whose scale decision falls within the accumulation error bound of
+// a boundary are recomputed exactly first.
 template <int FMT>
-__device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, const f32x16& aab, const uint16_t* T, int p,
-                                                int C, const XTile& x, float g, float* lds, int lane,
+__device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, const uint16_t* T, int p, int C,
+                                                const XTile& x, float g, float* lds, int lane,
                                                 uint32_t& scale_bits, uint32_t& n_exact) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   float amax = max_abs16(acc);
-  float aabs = max16(aab);
-  if (G == 32) {
-    amax = max_halves(amax);
-    aabs = max_halves(aabs);
-  }
-  const float d = err_bound(aabs, amax);
+  if (G == 32) amax = max_halves(amax);
+  const float d = err_bound(bound, amax);
   bool unsure;
-  if (FMT == kMXFP4) unsure = mx_unsure(amax, d);
-  else if (FMT == kINT4) unsure = int4_unsure(amax, d);
-  else unsure = nv_unsure(amax, d, g);
+  if (FMT == kMXFP4) {
+    // The E8M0 code depends only on the exponent field of amax.  It is
+    // settled when amax - d and amax + d share sign and exponent field.
+    unsure = (__float_as_uint(amax - d) ^ __float_as_uint(amax + d)) > 0x007FFFFFu;
+  } else if (FMT == kINT4) {
+    unsure = int4_unsure(amax, d);
+  } else {
+    unsure = nv_unsure(amax, d, g);
+  }
   uint64_t pending = __ballot(unsure);
   if (pending) {
     while (pending) {
@@ -369,10 +372,12 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, const f32x16& aab, 
     if (G == 32) amax = max_halves(amax);
   }
   if (FMT == kMXFP4) {
-    uint32_t code = (uint32_t)e8m0_code(amax);
-    scale_bits = code;
-    // the E8M0 code is the biased exponent of 2^e: pass it as an fp32
-    return pack_e2m1(acc, __uint_as_float(code << 23));
+    // 2^e with e = floor(log2 amax) - 2, clamped at 2^-127 (code 0): the
+    // exponent field minus 2.  Non-negative floats compare like integers.
+    const int eb = (int)(__float_as_uint(amax) & 0x7F800000u) - (2 << 23);
+    const uint32_t sc = (uint32_t)(eb > 0 ? eb : 0);
+    scale_bits = sc >> 23;
+    return pack_e2m1(acc, __uint_as_float(sc));
   } else if (FMT == kINT4) {
     uint32_t sb = f16_bits(amax / 7.0f);
     float s = f16_value(sb);
@@ -394,167 +399,253 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, const f32x16& aab, 
   }
 }
 
+// Largest |T| entry of the panel held by this wave, as a float.
+__device__ __forceinline__ float panel_tmax(const Frag& f) {
+  uint32_t m = 0;
+  const u32x4 w[2] = {f.t0, f.t1};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t lo = w[k][e] & 0x7FFFu, hi = (w[k][e] >> 16) & 0x7FFFu;
+      m = m > lo ? m : lo;
+      m = m > hi ? m : hi;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t v = (uint32_t)__shfl_xor((int)m, o, 64);
+    m = m > v ? m : v;
+  }
+  return __uint_as_float(m << 16);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- quant kernel
 //
-// Workgroup tile: 32 tokens x kPanels panels (256 channels).  Wave w owns
-// panels 2w and 2w+1 of the tile and keeps their T fragments in VGPRs for
-// all the tiles the workgroup walks.
+// Workgroup: 8 waves and a tile of 32 tokens x 8 panels (256 channels).
+// Wave w owns panel w of the tile and keeps its T fragment in VGPRs.  The
+// workgroup walks TPW consecutive 32-token tiles down its 256-channel column.
 //
-// Per tile:
-//  1. The X tile (32 rows x 512 B) arrives through row-contiguous 16-byte
-//     loads: one wave instruction covers 2 rows x 512 B.  It is prefetched
-//     into registers one tile ahead, then written to LDS (rows padded to
-//     528 B, so the transposing reads below are bank-conflict free).
-//  2. Each wave reads its panels' MFMA B fragments from LDS, contracts,
-//     quantizes, and writes codes and scales into LDS output tiles.
-//  3. The output tiles leave as full rows: 32 rows x 128 B of codes (one
-//     16-byte store per thread) and 32 rows x 8..16 B of scales.
+//  1. At entry every thread issues all of its activation loads for all TPW
+//     tiles: 2 x 16 B per tile, row-contiguous, so one wave instruction
+//     covers 2 rows x 512 B.  Nothing waits between loads, and the memory
+//     system sees the workgroup's whole footprint at once.
+//  2. Per tile, the data goes to LDS (rows padded to 528 B, so the
+//     transposing MFMA-operand reads are free of bank conflicts).  Each wave
+//     contracts its panel and quantizes, and codes and scales go to LDS
+//     output tiles.
+//  3. The output tiles leave as whole rows: 32 rows x 128 B of codes and
+//     32 rows x 8..16 B of scales.
 // Rows past M are loaded from row M-1 and not stored.  Channels past K
-// (the last tile of a row) are not loaded; they are zero in LDS.
+// are not loaded; they are zero in LDS, and T is zero there too.
 
-constexpr int kPanels = 8;            // panels (32 channels each) per workgroup tile
+constexpr int kQWaves = 8;            // waves per quant workgroup (one panel each)
+constexpr int kPanels = kQWaves;      // panels (32 channels each) per tile
 constexpr int kXRow = 512 + 16;       // LDS bytes per X row (256 bf16 + pad)
 constexpr int kCRow = 128 + 16;       // LDS bytes per code row (8 panels x 16 B + pad)
 constexpr int kSRow = 16;             // LDS bytes per scale row
 
-template <int FMT>
-__global__ __launch_bounds__(kWaves * 64) void quant_kernel(QuantArgs a) {
-  constexpr int G = (FMT == kNVFP4) ? 16 : 32;
-  __shared__ __attribute__((aligned(16))) uint8_t xs[32 * kXRow];
-  __shared__ __attribute__((aligned(16))) uint8_t cs[32 * kCRow];
-  __shared__ __attribute__((aligned(16))) uint8_t ss[32 * kSRow];
-  __shared__ float lds_y[kWaves][32];
+// LDS tiles of one quant workgroup.
+struct QuantLds {
+  uint8_t xs[2][32 * kXRow];  // activation tiles, double-buffered
+  uint8_t cs[2][32 * kCRow];  // code tiles, double-buffered
+  uint8_t ss[2][32 * kSRow];  // scale tiles, double-buffered
+  float y[kQWaves][32];       // exact-recompute exchange, per wave
+};
 
+// Contract and quantize panel `wave` of the staged tile.  Codes and scales
+// go to the LDS output tiles.
+//
+// The accumulation bound: for MXFP4, whose scale boundaries are powers of
+// two, the cheap bound tmax * sum_j |x_j| suffices.  Its MFMA has every row
+// of A equal to one, so every output row holds the token's L1 norm.  INT4
+// and NVFP4 scales have much denser boundaries, so they use the per-output
+// bound max_k sum_j |T_kj x_j| from an |T| x |x| MFMA.
+template <int FMT>
+__device__ __forceinline__ void panel_step(QuantLds& L, int buf, const Frag& f, float tmax, const uint16_t* T,
+                                           int p, int C, float g, int wave, int lane, uint32_t& n_exact) {
+  constexpr int G = (FMT == kNVFP4) ? 16 : 32;
+  const int n = lane & 31, h = lane >> 5;
+  const u32x4 mask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
+  XTile x;
+  const uint8_t* row = L.xs[buf] + n * kXRow + wave * 64 + 16 * h;
+  x.b0 = *reinterpret_cast<const u32x4*>(row);
+  x.b1 = *reinterpret_cast<const u32x4*>(row + 32);
+  f32x16 zero = {};
+  f32x16 acc = mfma32(f.t0, x.b0, zero);
+  acc = mfma32(f.t1, x.b1, acc);
+  float bound;
+  if (FMT == kMXFP4) {
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+    f32x16 l1 = mfma32(ones, x.b0 & mask, zero);
+    l1 = mfma32(ones, x.b1 & mask, l1);
+    bound = tmax * l1[0];
+  } else {
+    f32x16 aab = mfma32(f.t0 & mask, x.b0 & mask, zero);
+    aab = mfma32(f.t1 & mask, x.b1 & mask, aab);
+    bound = max16(aab);
+    if (G == 32) bound = max_halves(bound);
+  }
+  uint32_t sbits;
+  const u32x2 w = quantize_panel<FMT>(acc, bound, T, p, C, x, g, L.y[wave], lane, sbits, n_exact);
+  *reinterpret_cast<u32x2*>(L.cs[buf] + n * kCRow + wave * 16 + 8 * h) = w;
+  if (FMT == kMXFP4) {
+    if (h == 0) L.ss[buf][n * kSRow + wave] = (uint8_t)sbits;
+  } else if (FMT == kINT4) {
+    if (h == 0) *reinterpret_cast<uint16_t*>(L.ss[buf] + n * kSRow + 2 * wave) = (uint16_t)sbits;
+  } else {
+    L.ss[buf][n * kSRow + 2 * wave + h] = (uint8_t)sbits;
+  }
+}
+
+// FULL: every row of the run is below M, and K is a multiple of 256, so
+// every tile is complete and every scale row segment is 8- or 16-byte
+// aligned.  Addresses are then a uniform per-tile base (scalar registers)
+// plus a 32-bit per-lane offset fixed for the whole run.
+template <int FMT, int TPW, bool FULL>
+__device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds& L, int cg, int tg) {
+  constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
-  int cg, tg;
-  wg_coords(a.n_pg, a.n_tg, cg, tg);
   const int64_t K = a.K, M = a.M;
   const int C = (int)(K / G);
-  const int p0 = cg * kPanels;  // first panel of the tile
-  const int n_panels = (a.n_panels - p0 < kPanels) ? a.n_panels - p0 : kPanels;
+  const int p0 = cg * kPanels;
+  const int n_panels = FULL ? kPanels : ((a.n_panels - p0 < kPanels) ? a.n_panels - p0 : kPanels);
+  const int64_t tile0 = (int64_t)tg * TPW;
+  const int n_tiles = FULL ? TPW : (int)((a.n_tiles - tile0 < TPW) ? a.n_tiles - tile0 : TPW);
 
-  // T fragments of this wave's two panels (zero for panels past the end)
-  Frag f[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int pl = 2 * wave + j;
-    if (pl < n_panels) {
-      f[j] = load_t<G>(a.T, p0 + pl, C, lane);
-    } else {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      f[j] = Frag{z, z, z, z};
-    }
-  }
-
-  // Load mapping: instruction i (0..3) of thread t covers row 8i + t/32,
-  // 16-byte chunk t%32 of the 512-byte tile row.
+  // 1. activation loads, two tiles ahead.  Thread t covers 16-byte chunk
+  // t%32 of rows t/32 and t/32 + 16 of each 32-row tile.
   const int chunk = tid & 31;
-  const int64_t ch0 = (int64_t)p0 * 32 + 8 * chunk;  // first channel of this thread's chunk
-  const bool chunk_ok = ch0 < K;
-  const int64_t tile0 = (int64_t)tg * a.tiles_per_wave;
-  const int64_t tile1 = (tile0 + a.tiles_per_wave < a.n_tiles) ? tile0 + a.tiles_per_wave : a.n_tiles;
-
-  u32x4 pre[4];
-  auto load_tile = [&](int64_t t) {
+  const int row_a = tid >> 5;
+  const int64_t ch0 = (int64_t)p0 * 32 + 8 * chunk;
+  const bool chunk_ok = FULL || ch0 < K;
+  const uint16_t* fbase = a.X + tile0 * 32 * K + (int64_t)p0 * 32;  // FULL: uniform
+  const uint32_t foff = (uint32_t)(row_a * K + 8 * chunk);          // FULL: per lane
+  u32x4 pre[2][2];
+  auto issue = [&](int u, int slot) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = t * 32 + 8 * i + (tid >> 5);
-      const int64_t mc = m < M ? m : M - 1;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      pre[i] = chunk_ok ? load16_nt(a.X + mc * K + ch0) : z;
+    for (int i = 0; i < 2; ++i) {
+      if (FULL) {
+        pre[slot][i] = load16_nt(fbase + (int64_t)(32 * u + 16 * i) * K + foff);
+      } else {
+        const int64_t m = (tile0 + u) * 32 + row_a + 16 * i;
+        const int64_t mc = m < M ? m : M - 1;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        pre[slot][i] = (chunk_ok && u < n_tiles) ? load16_nt(a.X + mc * K + ch0) : z;
+      }
     }
   };
+  issue(0, 0);
+  if (TPW > 1) issue(1, 1);
+  const bool panel_ok = wave < n_panels;
+  Frag f;
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    f = panel_ok ? load_t<G>(a.T, p0 + wave, C, lane) : Frag{z, z, z, z};
+  }
+  const float tmax = (FMT == kMXFP4) ? panel_tmax(f) : 0.0f;
 
   float g = 0.0f;
   if (FMT == kNVFP4) g = *a.global_scale;
   uint32_t n_exact = 0;
-  const u32x4 mask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
-  const int n = lane & 31, h = lane >> 5;
 
-  // Valid bytes of a code row and of a scale row in this tile.
-  const int64_t code_bytes_left = K / 2 - (int64_t)p0 * 16;
-  const int code_row_bytes = (int)(code_bytes_left < kPanels * 16 ? code_bytes_left : kPanels * 16);
   const int s_elem = (FMT == kINT4) ? 2 : 1;
   const int64_t s_first = (G == 32) ? p0 : 2 * p0;  // first scale index of the tile in a row
-  const int s_count = (int)(((int64_t)C - s_first) < ((G == 32) ? kPanels : 2 * kPanels)
-                                ? (int64_t)C - s_first
-                                : ((G == 32) ? kPanels : 2 * kPanels));
+  const int s_max = (G == 32) ? kPanels : 2 * kPanels;
+  const int s_count = FULL ? s_max : (int)(((int64_t)C - s_first) < s_max ? (int64_t)C - s_first : s_max);
+  const int64_t code_bytes_left = K / 2 - (int64_t)p0 * 16;
+  const int code_row_bytes = FULL ? kPanels * 16 : (int)(code_bytes_left < kPanels * 16 ? code_bytes_left : kPanels * 16);
 
-  if (tile0 < tile1) load_tile(tile0);
-  for (int64_t t = tile0; t < tile1; ++t) {
-    // 1. stage the tile in LDS, start loading the next one
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(xs + (8 * i + (tid >> 5)) * kXRow + 16 * chunk) = pre[i];
-    if (t + 1 < tile1) load_tile(t + 1);
-    __syncthreads();
+  // output mapping: codes, thread t < 256 stores row t/8, 16-byte chunk t%8;
+  // scales, thread 256 + r stores row r.
+  const int c_row = (tid & 255) >> 3, c_chunk = tid & 7;
 
-    // 2. contract and quantize this wave's panels
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int pl = 2 * wave + j;
-      if (pl >= n_panels) break;
-      XTile x;
-      const uint8_t* row = xs + n * kXRow + pl * 64 + 16 * h;
-      x.b0 = *reinterpret_cast<const u32x4*>(row);
-      x.b1 = *reinterpret_cast<const u32x4*>(row + 32);
-      f32x16 zero = {};
-      f32x16 acc = mfma32(f[j].t0, x.b0, zero);
-      acc = mfma32(f[j].t1, x.b1, acc);
-      f32x16 aab = mfma32(f[j].t0 & mask, x.b0 & mask, zero);
-      aab = mfma32(f[j].t1 & mask, x.b1 & mask, aab);
-      uint32_t sbits;
-      const u32x2 w = quantize_panel<FMT>(acc, aab, a.T, p0 + pl, C, x, g, lds_y[wave], lane, sbits, n_exact);
-      *reinterpret_cast<u32x2*>(cs + n * kCRow + pl * 16 + 8 * h) = w;
-      if (FMT == kMXFP4) {
-        if (h == 0) ss[n * kSRow + pl] = (uint8_t)sbits;
-      } else if (FMT == kINT4) {
-        if (h == 0) *reinterpret_cast<uint16_t*>(ss + n * kSRow + 2 * pl) = (uint16_t)sbits;
-      } else {
-        ss[n * kSRow + 2 * pl + h] = (uint8_t)sbits;
+  auto stage = [&](int u) {  // tile u: registers -> xs[u & 1], refill with tile u + 2
+    uint8_t* xs = L.xs[u & 1];
+    *reinterpret_cast<u32x4*>(xs + row_a * kXRow + 16 * chunk) = pre[u & 1][0];
+    *reinterpret_cast<u32x4*>(xs + (row_a + 16) * kXRow + 16 * chunk) = pre[u & 1][1];
+    if (u + 2 < TPW) issue(u + 2, u & 1);
+  };
+  auto store = [&](int u) {  // tile u: cs/ss[u & 1] -> global, whole rows
+    const int64_t t = tile0 + u;
+    const uint8_t* cs = L.cs[u & 1];
+    const uint8_t* ss = L.ss[u & 1];
+    if (FULL) {
+      if (tid < 256) {
+        uint8_t* base = a.codes + (t * 32) * (K / 2) + (int64_t)p0 * 16;  // uniform
+        const uint32_t off = (uint32_t)(c_row * (K / 2) + 16 * c_chunk);
+        *reinterpret_cast<u32x4*>(base + off) = *reinterpret_cast<const u32x4*>(cs + c_row * kCRow + 16 * c_chunk);
+      } else if (tid < 288) {
+        const int r = tid - 256;
+        uint8_t* base = a.scales + ((t * 32) * C + s_first) * s_elem;  // uniform
+        const uint32_t off = (uint32_t)(r * C * s_elem);
+        if (s_max * s_elem == 8)
+          *reinterpret_cast<u32x2*>(base + off) = *reinterpret_cast<const u32x2*>(ss + r * kSRow);
+        else
+          *reinterpret_cast<u32x4*>(base + off) = *reinterpret_cast<const u32x4*>(ss + r * kSRow);
       }
-    }
-    __syncthreads();
-
-    // 3. write the tile's codes and scales as whole rows
-    {
-      const int r = tid >> 3, jc = tid & 7;  // row, 16-byte chunk
-      const int64_t m = t * 32 + r;
-      if (m < M && 16 * jc < code_row_bytes) {
-        uint8_t* dst = a.codes + m * (K / 2) + (int64_t)p0 * 16 + 16 * jc;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(cs + r * kCRow + 16 * jc);
-        if (16 * jc + 16 <= code_row_bytes) {
-          *reinterpret_cast<u32x4*>(dst) = v;
-        } else {  // a G=16 row ending half-way into the last panel
-          u32x2 h8 = {v[0], v[1]};
-          *reinterpret_cast<u32x2*>(dst) = h8;
+    } else {
+      if (tid < 256) {
+        const int64_t m = t * 32 + c_row;
+        if (m < M && 16 * c_chunk < code_row_bytes) {
+          uint8_t* dst = a.codes + m * (K / 2) + (int64_t)p0 * 16 + 16 * c_chunk;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(cs + c_row * kCRow + 16 * c_chunk);
+          if (16 * c_chunk + 16 <= code_row_bytes) {
+            *reinterpret_cast<u32x4*>(dst) = v;
+          } else {  // a G=16 row ending half-way into the last panel
+            u32x2 h8 = {v[0], v[1]};
+            *reinterpret_cast<u32x2*>(dst) = h8;
+          }
         }
-      }
-    }
-    if (tid < 32) {
-      const int64_t m = t * 32 + tid;
-      if (m < M) {
-        uint8_t* dst = a.scales + (m * C + s_first) * s_elem;
-        const uint8_t* src = ss + tid * kSRow;
-        const int nb = s_count * s_elem;
-        if (nb == 8 && ((uintptr_t)dst & 7) == 0) {
-          *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const u32x2*>(src);
-        } else if (nb == 16 && ((uintptr_t)dst & 15) == 0) {
-          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-        } else {
+      } else if (tid < 288) {
+        const int r = tid - 256;
+        const int64_t m = t * 32 + r;
+        if (m < M) {
+          uint8_t* dst = a.scales + (m * C + s_first) * s_elem;
+          const uint8_t* src = ss + r * kSRow;
+          const int nb = s_count * s_elem;
           for (int b = 0; b < nb; ++b) dst[b] = src[b];
         }
       }
     }
-    // the next iteration overwrites xs only after this barrier-free store
-    // phase; the barrier after its LDS writes orders the cs/ss reuse.
+  };
+
+  // One barrier per tile.  At barrier u: tile u is staged in xs[u & 1] and
+  // the codes of tile u - 1 are complete in cs[(u - 1) & 1].  After it, each
+  // wave contracts tile u, stages tile u + 1 into the other xs buffer and
+  // stores tile u - 1.  The xs buffer tile u + 1 overwrites was last read by
+  // the contraction of tile u - 1, which finished before barrier u.  The cs
+  // buffer tile u writes was last read by the store of tile u - 2, which
+  // finished before barrier u.
+  stage(0);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    if (!FULL && u >= n_tiles) break;
+    if (panel_ok) panel_step<FMT>(L, u & 1, f, tmax, a.T, p0 + wave, C, g, wave, lane, n_exact);
+    if (u >= 1) store(u - 1);
+    if (u + 1 < TPW && (FULL || u + 1 < n_tiles)) stage(u + 1);
     __syncthreads();
   }
+  {
+    const int last = FULL ? TPW - 1 : n_tiles - 1;
+    if (last >= 0) store(last);
+  }
   if (a.n_exact && n_exact) atomicAdd(a.n_exact, n_exact);
+}
+
+template <int FMT, int TPW>
+__global__ __launch_bounds__(kQWaves * 64) void quant_kernel(QuantArgs a) {
+  __shared__ __attribute__((aligned(16))) QuantLds L;
+  int cg, tg;
+  wg_coords(a.n_pg, a.n_tg, cg, tg);
+  const bool full = ((int64_t)(tg + 1) * TPW * 32 <= a.M) && (a.K % (kPanels * 32) == 0);
+  if (full) quant_run<FMT, TPW, true>(a, L, cg, tg);
+  else quant_run<FMT, TPW, false>(a, L, cg, tg);
 }
 
 // ---------------------------------------------------------------- transform / absmax
@@ -631,7 +722,14 @@ __global__ void e2m1_kernel(const float* __restrict__ v, int64_t n, uint8_t* __r
 
 template <int FMT>
 static hipError_t launch_quant_fmt(const QuantArgs& a, int n_wg, hipStream_t s) {
-  hipLaunchKernelGGL((quant_kernel<FMT>), dim3(n_wg), dim3(kWaves * 64), 0, s, a);
+  dim3 grid(n_wg), block(kQWaves * 64);
+  switch (a.tiles_per_wave) {
+    case 1: hipLaunchKernelGGL((quant_kernel<FMT, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((quant_kernel<FMT, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((quant_kernel<FMT, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((quant_kernel<FMT, 8>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
