@@ -13,9 +13,12 @@ scales written once) divided by the time per step, in GB/s.  Cold cache:
 the steps rotate through buffer sets whose total footprint is more than
 twice the 256 MB Infinity Cache, so each step reads its inputs from HBM.
 
-Printed: one JSON line.  It carries the roofline of the kernel (average
-kernel duration from HIP events around each launch), and the CPU oracle
-timed on the host as a reported baseline.
+Printed: one JSON line.  It carries the roofline of the kernel (its
+average duration over the timed region, HIP events on the launch stream),
+HBM traffic from the counter profile when one matches the kernel source,
+context numbers (the same kernel with hot caches, a plain device copy of
+the same bytes), and the CPU oracle timed on the host as a reported
+baseline.
 """
 
 from __future__ import annotations
@@ -53,6 +56,11 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the path, run a plain device copy of this many MiB --steps times "
                          "(reference for the HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="instead of running, read four rocprofv3 --pmc output folders (FETCH_SIZE and "
+                         "WRITE_SIZE of the path, then of --copy-probe-mib) and write "
+                         "profiles/traffic_<workload>.json")
+    ap.add_argument("--traffic-cmds", default="", help="the commands that made the --traffic-from folders")
     return ap.parse_args()
 
 
@@ -73,6 +81,92 @@ def copy_probe(mib: int, steps: int) -> None:
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "steps": steps,
                       "ms_per_copy": round(ms, 6), "GBps_read_plus_write": round(2 * n / ms / 1e6, 2)}),
           flush=True)
+
+
+def _pmc_rows(folder: str, counter: str):
+    """(kernel name, value) of every dispatch in a rocprofv3 --pmc output
+    folder (SQLite results database or counter_collection.csv)."""
+    import csv
+    import glob
+
+    rows = []
+    dbs = glob.glob(os.path.join(folder, "**", "*_results.db"), recursive=True)
+    if dbs:  # rocprofv3's default SQLite output: the counters_collection view
+        import sqlite3
+
+        for fn in dbs:
+            con = sqlite3.connect(fn)
+            rows += [(k, float(v)) for k, v in con.execute(
+                "select kernel_name, value from counters_collection where counter_name = ?", (counter,))]
+            con.close()
+        return rows
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no rocprofv3 output under %s" % folder)
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def _median_for(rows, pick):
+    import statistics
+
+    vals = [v for k, v in rows if pick(k)]
+    if not vals:
+        raise SystemExit("no matching dispatches")
+    return statistics.median(vals), len(vals)
+
+
+def ingest_traffic(args) -> None:
+    """HBM bytes per launch of the quant kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for a
+    plain device copy of known size."""
+    from synthetic import CONFIGS
+
+    wl = CONFIGS[args.workload]
+    fdir, wdir, cfdir, cwdir = args.traffic_from
+    is_quant = lambda k: "quant_kernel" in k
+    is_copy = lambda k: "copy" in k.lower()
+    f_kib, nf = _median_for(_pmc_rows(fdir, "FETCH_SIZE"), is_quant)
+    w_kib, nw = _median_for(_pmc_rows(wdir, "WRITE_SIZE"), is_quant)
+    cf_kib, _ = _median_for(_pmc_rows(cfdir, "FETCH_SIZE"), is_copy)
+    cw_kib, _ = _median_for(_pmc_rows(cwdir, "WRITE_SIZE"), is_copy)
+    copy_bytes = args.copy_probe_mib << 20
+    if copy_bytes <= 0:
+        raise SystemExit("--copy-probe-mib must give the size of the calibration copy")
+    ff = copy_bytes / (cf_kib * 1024.0)
+    fw = copy_bytes / (cw_kib * 1024.0)
+    rd = f_kib * 1024.0 * ff
+    wr = w_kib * 1024.0 * fw
+    alg = algorithmic_bytes(wl.fmt, wl.M, wl.K, wl.G)
+    alg_rd = wl.M * wl.K * 2 + (wl.K // wl.G) * wl.G * wl.G * 2
+    out = {
+        "workload": wl.name,
+        "kernel": "quant_kernel<%s>" % wl.fmt,
+        "kernel_source_sha": _kernel_source_sha(),
+        "hbm_bytes_per_launch": round(rd + wr),
+        "read_bytes_per_launch": round(rd),
+        "write_bytes_per_launch": round(wr),
+        "algorithmic_bytes_per_launch": alg,
+        "algorithmic_read_bytes": alg_rd,
+        "algorithmic_write_bytes": alg - alg_rd,
+        "traffic_over_algorithmic": round((rd + wr) / alg, 4),
+        "raw_FETCH_SIZE_KiB_median": f_kib,
+        "raw_WRITE_SIZE_KiB_median": w_kib,
+        "dispatches": [nf, nw],
+        "calibration": {"copy_bytes_each_way": copy_bytes, "copy_FETCH_SIZE_KiB": cf_kib,
+                        "copy_WRITE_SIZE_KiB": cw_kib, "fetch_factor": round(ff, 4),
+                        "write_factor": round(fw, 4)},
+        "commands": args.traffic_cmds,
+    }
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def cpu_baseline(wl, x_bits_np, t_bits_np, seconds: float):
@@ -127,6 +221,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.traffic_from:
+        ingest_traffic(args)
+        return
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, args.steps)
         return
@@ -180,13 +277,12 @@ def main():
         if st:
             _lib.check(st, "wush_quant")
 
-    # Warmup: W untimed steps.
-    for i in range(args.warmup):
+    for i in range(min(args.warmup, 8)):  # first launches: code upload, clocks
         launch(i)
     torch.cuda.synchronize()
 
-    # Per-launch kernel durations from HIP events on the launch stream.
-    # These give the kernel's average duration for the roofline.
+    # Per-launch kernel durations from HIP events on the launch stream, a
+    # diagnostic: the events between launches add their own cost.
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -219,6 +315,13 @@ def main():
             if g is not None:
                 g.replay()
         torch.cuda.synchronize()
+    # Warmup: W untimed steps, directly before the timed region.
+    if args.mode == "graph" and args.warmup:
+        wg = capture(args.warmup)
+        wg.replay()
+    else:
+        for i in range(args.warmup):
+            launch(i)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -238,8 +341,43 @@ def main():
     ms_per_step = ms_total / args.steps
 
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    kern_avg_ms = float(kern_ms.mean())
+    # The roofline uses the kernel's average duration over the timed region:
+    # back-to-back launches of the one kernel, HIP events on the launch
+    # stream.  rocprofv3 --kernel-trace on the same command reports the
+    # per-dispatch duration without the fixed inter-kernel gap (about
+    # 1.5 us on this platform, measured with an empty kernel).  The
+    # profile summaries under profiles/ record both.
+    kern_avg_ms = ms_per_step
     achieved = nbytes / (kern_avg_ms * 1e-3) / 1e9
+
+    # Context, not the metric: the same kernel on one buffer set (inputs
+    # served from the Infinity Cache), and a plain device copy moving the
+    # same number of bytes, cold, as the achievable streaming reference.
+    def graph_ms(fn, n, reps):
+        cap = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(n):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (n * reps)
+
+    hot_ms = graph_ms(lambda i: launch(0), 64, 4)
+    # The copy moves the activation bytes themselves (the first half of each
+    # set's X), since bandwidth on this part depends on the data.
+    half = min(nbytes // 2, M * K * 2) // 16 * 16
+    csets = [(X.view(torch.uint8).view(-1)[:half], torch.empty(half, dtype=torch.uint8, device=dev))
+             for X, _, _, _ in sets]
+    copy_ms = graph_ms(lambda i: csets[i % n_sets][1].copy_(csets[i % n_sets][0]), n_sets * 4, 4)
+    del csets
+    torch.cuda.synchronize()
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name)
@@ -286,9 +424,16 @@ def main():
             "traffic": traffic,
             "kernel": "quant_kernel<%s>" % fmt,
             "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
-            "kernel_p10_p90_us": [round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
-                                  round(float(np.percentile(kern_ms, 90)) * 1e3, 3)],
+            "per_launch_event_avg_us": round(float(kern_ms.mean()) * 1e3, 3),
+            "per_launch_event_p10_p90_us": [round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
+                                            round(float(np.percentile(kern_ms, 90)) * 1e3, 3)],
         },
+    }
+    out["context"] = {
+        "hot_cache_us_per_step": round(hot_ms * 1e3, 3),
+        "hot_cache_GBps": round(nbytes / (hot_ms * 1e-3) / 1e9, 2),
+        "device_copy_cold": {"bytes_read_plus_written": 2 * half, "us": round(copy_ms * 1e3, 3),
+                             "GBps": round(2 * half / (copy_ms * 1e-3) / 1e9, 2)},
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle (~%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)

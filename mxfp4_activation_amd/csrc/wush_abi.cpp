@@ -85,23 +85,23 @@ void plan(int64_t M, int64_t K, int64_t* n_tiles, int64_t* tpw, int* n_panels, i
 }
 
 // Quant kernel split: a workgroup (8 waves) owns a 256-channel column of
-// the input and walks a run of TPW 32-token tiles down it, with all of the
-// run's loads issued at entry.  TPW (1, 2, 4 or 8) is the longest run that
-// still gives at least 512 workgroups (two per CU, all resident at once), so
-// short batches still spread over every CU.  WUSH_TILES_PER_WG overrides
-// it for tuning.
+// the input and a run of TPW 32-token tiles, all loaded at entry.  TPW
+// (1, 2 or 4) is the longest run that still gives at least 1024 workgroups
+// (four per CU), so that several workgroups share each CU and cover each
+// other's waits; longer runs amortize the T fragment loads on big batches.
+// WUSH_TILES_PER_WG overrides it for tuning.
 void plan_quant(int64_t M, int64_t K, int64_t* n_tiles, int64_t* tpw, int* n_panels, int* n_pg, int* n_tg) {
   *n_tiles = (M + 31) / 32;
   *n_panels = (int)((K + 31) / 32);
   *n_pg = (*n_panels + wush::kPanelsPerTile - 1) / wush::kPanelsPerTile;
-  const int64_t target_wg = 512;
-  int64_t t = 8;
+  const int64_t target_wg = 1024;
+  int64_t t = 4;
   while (t > 1 && (int64_t)(*n_pg) * ((*n_tiles + t - 1) / t) < target_wg) t >>= 1;
   static const int64_t env = [] {
     const char* s = getenv("WUSH_TILES_PER_WG");
     return s ? (int64_t)atoll(s) : (int64_t)0;
   }();
-  if (env == 1 || env == 2 || env == 4 || env == 8) t = env;
+  if (env == 1 || env == 2 || env == 4) t = env;
   *tpw = t;
   *n_tg = (int)((*n_tiles + t - 1) / t);
 }

@@ -19,10 +19,11 @@
 //    accumulator registers 0..15.  A 32-group's AbsMax is then an in-lane max
 //    plus one exchange between lanes l and l^32.  A 16-group (NVFP4, with a
 //    block-diagonal pair as A) is entirely in-lane.
-//  * Exact scales.  A second MFMA pair computes A_i = sum_j |T_ij||x_j|,
-//    which bounds how far the fp32 accumulation can be from the exact sum.
-//    If a group's scale decision is not constant over
-//    [amax - d, amax + d], the wave recomputes that token's panel in
+//  * Exact scales.  A second MFMA pair bounds sum_j |T_ij||x_j| (MXFP4:
+//    max|T| times the token's L1 norm; INT4 and NVFP4: the exact per-output
+//    sums from |T| x |x|), which bounds how far the fp32 accumulation can
+//    be from the exact sum.  If a group's scale decision is not constant
+//    over [amax - d, amax + d], the wave recomputes that token's panel in
 //    float64.  The result is then the exactly rounded y.
 //
 // Memory layout and ABI: see include/wush.h.
@@ -217,28 +218,16 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // Recompute token `n`'s 32 outputs of the current panel in float64 and
 // write them into the accumulator of lanes (n, 0) and (n, 1).  Lane (i, h)
-// owns output row permuted_row(i).  It re-reads its half-row of T and forms
-// the half-h partial sum; lane l ^ 32 holds the other half.  The reads are
-// volatile, so the compiler cannot hoist this rare path's float64 copies of
-// T into registers that stay live across the hot loop.
-template <int G>
-__device__ __forceinline__ void exact_panel(int n, const uint16_t* T, int p, int C, const XTile& x, f32x16& acc,
-                                         float* lds, int lane) {
+// owns output row permuted_row(i): its T fragment (the MFMA A operand) is
+// exactly its half-row of T, and it forms the half-h partial sum; lane
+// l ^ 32 holds the other half.  The fragment is copied through an empty asm
+// statement, so the compiler cannot hoist this rare path's float64
+// conversions of T out of the hot loop into registers that stay live.
+__device__ __forceinline__ void exact_panel(int n, const Frag& f, const XTile& x, f32x16& acc, float* lds, int lane) {
   const int i = lane & 31, h = lane >> 5;
   const int row = permuted_row(i);
-  u32x4 tk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-  if (G == 32) {
-    const uint16_t* src = T + ((size_t)p * 32 + row) * 32 + 8 * h;
-    tk[0] = *reinterpret_cast<const volatile u32x4*>(src);
-    tk[1] = *reinterpret_cast<const volatile u32x4*>(src + 16);
-  } else {
-    const int kk = row >> 4, blk = 2 * p + kk;
-    if (blk < C) {
-      u32x4 t = *reinterpret_cast<const volatile u32x4*>(T + (size_t)blk * 256 + (row & 15) * 16 + 8 * h);
-      if (kk == 0) tk[0] = t;
-      else tk[1] = t;
-    }
-  }
+  u32x4 tk[2] = {f.t0, f.t1};
+  asm volatile("" : "+v"(tk[0]), "+v"(tk[1]));
   const u32x4 bk[2] = {x.b0, x.b1};
   double s = 0.0;
 #pragma unroll
@@ -343,7 +332,7 @@ __device__ __forceinline__ void wg_coords(int n_pg, int n_tg, int& pg, int& tg) 
 // Groups whose scale decision falls within the accumulation error bound of
 // a boundary are recomputed exactly first.
 template <int FMT>
-__device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, const uint16_t* T, int p, int C,
+__device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, const Frag& f,
                                                 const XTile& x, float g, float* lds, int lane,
                                                 uint32_t& scale_bits, uint32_t& n_exact) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
@@ -364,7 +353,7 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, const 
   if (pending) {
     while (pending) {
       int ln = __builtin_ctzll(pending) & 31;
-      exact_panel<G>(ln, T, p, C, x, acc, lds, lane);
+      exact_panel(ln, f, x, acc, lds, lane);
       pending &= ~((1ull << ln) | (1ull << (ln + 32)));
       n_exact += (lane == 0) ? 1u : 0u;
     }
@@ -424,39 +413,43 @@ __device__ __forceinline__ float panel_tmax(const Frag& f) {
 
 // ---------------------------------------------------------------- quant kernel
 //
-// Workgroup: 8 waves and a tile of 32 tokens x 8 panels (256 channels).
-// Wave w owns panel w of the tile and keeps its T fragment in VGPRs.  The
-// workgroup walks TPW consecutive 32-token tiles down its 256-channel column.
+// Workgroup: 8 waves and a column of 256 channels (8 panels) over TPW
+// consecutive 32-token tiles.  Wave w owns panel w and keeps its T fragment
+// in VGPRs.
 //
-//  1. At entry every thread issues all of its activation loads for all TPW
-//     tiles: 2 x 16 B per tile, row-contiguous, so one wave instruction
-//     covers 2 rows x 512 B.  Nothing waits between loads, and the memory
-//     system sees the workgroup's whole footprint at once.
-//  2. Per tile, the data goes to LDS (rows padded to 528 B, so the
-//     transposing MFMA-operand reads are free of bank conflicts).  Each wave
-//     contracts its panel and quantizes, and codes and scales go to LDS
-//     output tiles.
-//  3. The output tiles leave as whole rows: 32 rows x 128 B of codes and
-//     32 rows x 8..16 B of scales.
+//  1. At entry each wave loads its T fragment, then every thread issues all
+//     of its activation loads for the TPW tiles: 2 x 16 B per tile,
+//     row-contiguous, so one wave instruction covers 2 rows x 512 B.
+//  2. The tiles go to LDS (rows padded to 528 B, so the transposing
+//     MFMA-operand reads are free of bank conflicts), then one barrier.
+//  3. Each wave contracts and quantizes its panel of every tile.  It writes
+//     the codes back in place over the first 16 B of its own panel in each
+//     row (only this wave reads those bytes), and the scales into the row's
+//     16-byte pad.  Then a second barrier.
+//  4. The output leaves as whole rows: 32 rows x 128 B of codes and
+//     32 rows x 8..16 B of scales per tile.
+//
+// One barrier per workgroup for the data, rather than one per tile: a
+// barrier makes the whole workgroup wait for its slowest wave's loads, and
+// with several workgroups resident per CU one workgroup's wait is covered
+// by another's work.
 // Rows past M are loaded from row M-1 and not stored.  Channels past K
 // are not loaded; they are zero in LDS, and T is zero there too.
 
 constexpr int kQWaves = 8;            // waves per quant workgroup (one panel each)
 constexpr int kPanels = kQWaves;      // panels (32 channels each) per tile
-constexpr int kXRow = 512 + 16;       // LDS bytes per X row (256 bf16 + pad)
-constexpr int kCRow = 128 + 16;       // LDS bytes per code row (8 panels x 16 B + pad)
-constexpr int kSRow = 16;             // LDS bytes per scale row
+constexpr int kXRow = 512 + 16;       // LDS bytes per row: 256 bf16, then 16 B of scales
+constexpr int kScaleOff = 512;        // scales of a row start here
 
-// LDS tiles of one quant workgroup.
+// LDS of one quant workgroup.
+template <int TPW>
 struct QuantLds {
-  uint8_t xs[2][32 * kXRow];  // activation tiles, double-buffered
-  uint8_t cs[2][32 * kCRow];  // code tiles, double-buffered
-  uint8_t ss[2][32 * kSRow];  // scale tiles, double-buffered
-  float y[kQWaves][32];       // exact-recompute exchange, per wave
+  uint8_t xs[TPW][32 * kXRow];  // activation tiles; codes and scales in place
+  float y[kQWaves][32];         // exact-recompute exchange, per wave
 };
 
-// Contract and quantize panel `wave` of the staged tile.  Codes and scales
-// go to the LDS output tiles.
+// Contract and quantize panel `wave` of one staged tile; write its codes and
+// scales back into the tile.
 //
 // The accumulation bound: for MXFP4, whose scale boundaries are powers of
 // two, the cheap bound tmax * sum_j |x_j| suffices.  Its MFMA has every row
@@ -464,15 +457,15 @@ struct QuantLds {
 // and NVFP4 scales have much denser boundaries, so they use the per-output
 // bound max_k sum_j |T_kj x_j| from an |T| x |x| MFMA.
 template <int FMT>
-__device__ __forceinline__ void panel_step(QuantLds& L, int buf, const Frag& f, float tmax, const uint16_t* T,
-                                           int p, int C, float g, int wave, int lane, uint32_t& n_exact) {
+__device__ __forceinline__ void panel_step(uint8_t* xs, float* ybuf, const Frag& f, float tmax, float g, int wave,
+                                           int lane, uint32_t& n_exact) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   const int n = lane & 31, h = lane >> 5;
   const u32x4 mask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
   XTile x;
-  const uint8_t* row = L.xs[buf] + n * kXRow + wave * 64 + 16 * h;
-  x.b0 = *reinterpret_cast<const u32x4*>(row);
-  x.b1 = *reinterpret_cast<const u32x4*>(row + 32);
+  uint8_t* row = xs + n * kXRow;
+  x.b0 = *reinterpret_cast<const u32x4*>(row + wave * 64 + 16 * h);
+  x.b1 = *reinterpret_cast<const u32x4*>(row + wave * 64 + 16 * h + 32);
   f32x16 zero = {};
   f32x16 acc = mfma32(f.t0, x.b0, zero);
   acc = mfma32(f.t1, x.b1, acc);
@@ -489,23 +482,25 @@ __device__ __forceinline__ void panel_step(QuantLds& L, int buf, const Frag& f, 
     if (G == 32) bound = max_halves(bound);
   }
   uint32_t sbits;
-  const u32x2 w = quantize_panel<FMT>(acc, bound, T, p, C, x, g, L.y[wave], lane, sbits, n_exact);
-  *reinterpret_cast<u32x2*>(L.cs[buf] + n * kCRow + wave * 16 + 8 * h) = w;
+  const u32x2 w = quantize_panel<FMT>(acc, bound, f, x, g, ybuf, lane, sbits, n_exact);
+  // Every lane of the wave has read its operands before any lane writes:
+  // the reads above feed the MFMAs whose results the writes depend on.
+  *reinterpret_cast<u32x2*>(row + wave * 64 + 8 * h) = w;
   if (FMT == kMXFP4) {
-    if (h == 0) L.ss[buf][n * kSRow + wave] = (uint8_t)sbits;
+    if (h == 0) row[kScaleOff + wave] = (uint8_t)sbits;
   } else if (FMT == kINT4) {
-    if (h == 0) *reinterpret_cast<uint16_t*>(L.ss[buf] + n * kSRow + 2 * wave) = (uint16_t)sbits;
+    if (h == 0) *reinterpret_cast<uint16_t*>(row + kScaleOff + 2 * wave) = (uint16_t)sbits;
   } else {
-    L.ss[buf][n * kSRow + 2 * wave + h] = (uint8_t)sbits;
+    row[kScaleOff + 2 * wave + h] = (uint8_t)sbits;
   }
 }
 
-// FULL: every row of the run is below M, and K is a multiple of 256, so
-// every tile is complete and every scale row segment is 8- or 16-byte
-// aligned.  Addresses are then a uniform per-tile base (scalar registers)
-// plus a 32-bit per-lane offset fixed for the whole run.
+// FULL: every row of the run is below M, K is a multiple of 256 and at most
+// 2^26, so every tile is complete, every scale row segment is 8- or 16-byte
+// aligned, and per-lane offsets fit in 32 bits.  Addresses are then a
+// uniform per-tile base (scalar registers) plus a per-lane offset.
 template <int FMT, int TPW, bool FULL>
-__device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds& L, int cg, int tg) {
+__device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, int cg, int tg) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -517,87 +512,97 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds& L, int c
   const int64_t tile0 = (int64_t)tg * TPW;
   const int n_tiles = FULL ? TPW : (int)((a.n_tiles - tile0 < TPW) ? a.n_tiles - tile0 : TPW);
 
-  // 1. activation loads, two tiles ahead.  Thread t covers 16-byte chunk
-  // t%32 of rows t/32 and t/32 + 16 of each 32-row tile.
-  const int chunk = tid & 31;
-  const int row_a = tid >> 5;
-  const int64_t ch0 = (int64_t)p0 * 32 + 8 * chunk;
-  const bool chunk_ok = FULL || ch0 < K;
-  const uint16_t* fbase = a.X + tile0 * 32 * K + (int64_t)p0 * 32;  // FULL: uniform
-  const uint32_t foff = (uint32_t)(row_a * K + 8 * chunk);          // FULL: per lane
-  u32x4 pre[2][2];
-  auto issue = [&](int u, int slot) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (FULL) {
-        pre[slot][i] = load16_nt(fbase + (int64_t)(32 * u + 16 * i) * K + foff);
-      } else {
-        const int64_t m = (tile0 + u) * 32 + row_a + 16 * i;
-        const int64_t mc = m < M ? m : M - 1;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        pre[slot][i] = (chunk_ok && u < n_tiles) ? load16_nt(a.X + mc * K + ch0) : z;
-      }
-    }
-  };
-  issue(0, 0);
-  if (TPW > 1) issue(1, 1);
+  // 1. T fragment first, then every activation load of the run.  The
+  // memory counter retires in order, so the wave can use T while the
+  // activations are still in flight.
   const bool panel_ok = wave < n_panels;
   Frag f;
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
     f = panel_ok ? load_t<G>(a.T, p0 + wave, C, lane) : Frag{z, z, z, z};
   }
+  // Thread t covers 16-byte chunk t%32 of rows t/32 and t/32 + 16 of each tile.
+  const int chunk = tid & 31;
+  const int row_a = tid >> 5;
+  const int64_t ch0 = (int64_t)p0 * 32 + 8 * chunk;
+  const bool chunk_ok = FULL || ch0 < K;
+  u32x4 v[TPW][2];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (FULL) {
+        const uint16_t* base = a.X + (tile0 + u) * 32 * K + (int64_t)p0 * 32;  // uniform
+        v[u][i] = load16_nt(base + (uint32_t)((row_a + 16 * i) * K + 8 * chunk));
+      } else {
+        const int64_t m = (tile0 + u) * 32 + row_a + 16 * i;
+        const int64_t mc = m < M ? m : M - 1;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        v[u][i] = (chunk_ok && u < n_tiles) ? load16_nt(a.X + mc * K + ch0) : z;
+      }
+    }
+  }
   const float tmax = (FMT == kMXFP4) ? panel_tmax(f) : 0.0f;
-
   float g = 0.0f;
   if (FMT == kNVFP4) g = *a.global_scale;
-  uint32_t n_exact = 0;
 
+  // 2. stage, in arrival order
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    *reinterpret_cast<u32x4*>(L.xs[u] + row_a * kXRow + 16 * chunk) = v[u][0];
+    *reinterpret_cast<u32x4*>(L.xs[u] + (row_a + 16) * kXRow + 16 * chunk) = v[u][1];
+  }
+  __syncthreads();
+
+  // 3. contract and quantize
+  uint32_t n_exact = 0;
+  if (panel_ok) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (!FULL && u >= n_tiles) break;
+      panel_step<FMT>(L.xs[u], L.y[wave], f, tmax, g, wave, lane, n_exact);
+    }
+  }
+  __syncthreads();
+
+  // 4. whole-row stores: thread t < 256 stores 16 B of codes (row t/8,
+  // panel t%8), threads 256..287 store one row's scales.
   const int s_elem = (FMT == kINT4) ? 2 : 1;
   const int64_t s_first = (G == 32) ? p0 : 2 * p0;  // first scale index of the tile in a row
   const int s_max = (G == 32) ? kPanels : 2 * kPanels;
   const int s_count = FULL ? s_max : (int)(((int64_t)C - s_first) < s_max ? (int64_t)C - s_first : s_max);
   const int64_t code_bytes_left = K / 2 - (int64_t)p0 * 16;
   const int code_row_bytes = FULL ? kPanels * 16 : (int)(code_bytes_left < kPanels * 16 ? code_bytes_left : kPanels * 16);
-
-  // output mapping: codes, thread t < 256 stores row t/8, 16-byte chunk t%8;
-  // scales, thread 256 + r stores row r.
-  const int c_row = (tid & 255) >> 3, c_chunk = tid & 7;
-
-  auto stage = [&](int u) {  // tile u: registers -> xs[u & 1], refill with tile u + 2
-    uint8_t* xs = L.xs[u & 1];
-    *reinterpret_cast<u32x4*>(xs + row_a * kXRow + 16 * chunk) = pre[u & 1][0];
-    *reinterpret_cast<u32x4*>(xs + (row_a + 16) * kXRow + 16 * chunk) = pre[u & 1][1];
-    if (u + 2 < TPW) issue(u + 2, u & 1);
-  };
-  auto store = [&](int u) {  // tile u: cs/ss[u & 1] -> global, whole rows
+  const int c_row = (tid & 255) >> 3, c_panel = tid & 7;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    if (!FULL && u >= n_tiles) break;
     const int64_t t = tile0 + u;
-    const uint8_t* cs = L.cs[u & 1];
-    const uint8_t* ss = L.ss[u & 1];
+    const uint8_t* xs = L.xs[u];
     if (FULL) {
       if (tid < 256) {
         uint8_t* base = a.codes + (t * 32) * (K / 2) + (int64_t)p0 * 16;  // uniform
-        const uint32_t off = (uint32_t)(c_row * (K / 2) + 16 * c_chunk);
-        *reinterpret_cast<u32x4*>(base + off) = *reinterpret_cast<const u32x4*>(cs + c_row * kCRow + 16 * c_chunk);
+        const uint32_t off = (uint32_t)(c_row * (K / 2) + 16 * c_panel);
+        *reinterpret_cast<u32x4*>(base + off) = *reinterpret_cast<const u32x4*>(xs + c_row * kXRow + 64 * c_panel);
       } else if (tid < 288) {
         const int r = tid - 256;
         uint8_t* base = a.scales + ((t * 32) * C + s_first) * s_elem;  // uniform
         const uint32_t off = (uint32_t)(r * C * s_elem);
         if (s_max * s_elem == 8)
-          *reinterpret_cast<u32x2*>(base + off) = *reinterpret_cast<const u32x2*>(ss + r * kSRow);
+          *reinterpret_cast<u32x2*>(base + off) = *reinterpret_cast<const u32x2*>(xs + r * kXRow + kScaleOff);
         else
-          *reinterpret_cast<u32x4*>(base + off) = *reinterpret_cast<const u32x4*>(ss + r * kSRow);
+          *reinterpret_cast<u32x4*>(base + off) = *reinterpret_cast<const u32x4*>(xs + r * kXRow + kScaleOff);
       }
     } else {
       if (tid < 256) {
         const int64_t m = t * 32 + c_row;
-        if (m < M && 16 * c_chunk < code_row_bytes) {
-          uint8_t* dst = a.codes + m * (K / 2) + (int64_t)p0 * 16 + 16 * c_chunk;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(cs + c_row * kCRow + 16 * c_chunk);
-          if (16 * c_chunk + 16 <= code_row_bytes) {
-            *reinterpret_cast<u32x4*>(dst) = v;
+        if (m < M && 16 * c_panel < code_row_bytes) {
+          uint8_t* dst = a.codes + m * (K / 2) + (int64_t)p0 * 16 + 16 * c_panel;
+          const u32x4 cv = *reinterpret_cast<const u32x4*>(xs + c_row * kXRow + 64 * c_panel);
+          if (16 * c_panel + 16 <= code_row_bytes) {
+            *reinterpret_cast<u32x4*>(dst) = cv;
           } else {  // a G=16 row ending half-way into the last panel
-            u32x2 h8 = {v[0], v[1]};
+            u32x2 h8 = {cv[0], cv[1]};
             *reinterpret_cast<u32x2*>(dst) = h8;
           }
         }
@@ -606,44 +611,22 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds& L, int c
         const int64_t m = t * 32 + r;
         if (m < M) {
           uint8_t* dst = a.scales + (m * C + s_first) * s_elem;
-          const uint8_t* src = ss + r * kSRow;
+          const uint8_t* src = xs + r * kXRow + kScaleOff;
           const int nb = s_count * s_elem;
           for (int b = 0; b < nb; ++b) dst[b] = src[b];
         }
       }
     }
-  };
-
-  // One barrier per tile.  At barrier u: tile u is staged in xs[u & 1] and
-  // the codes of tile u - 1 are complete in cs[(u - 1) & 1].  After it, each
-  // wave contracts tile u, stages tile u + 1 into the other xs buffer and
-  // stores tile u - 1.  The xs buffer tile u + 1 overwrites was last read by
-  // the contraction of tile u - 1, which finished before barrier u.  The cs
-  // buffer tile u writes was last read by the store of tile u - 2, which
-  // finished before barrier u.
-  stage(0);
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    if (!FULL && u >= n_tiles) break;
-    if (panel_ok) panel_step<FMT>(L, u & 1, f, tmax, a.T, p0 + wave, C, g, wave, lane, n_exact);
-    if (u >= 1) store(u - 1);
-    if (u + 1 < TPW && (FULL || u + 1 < n_tiles)) stage(u + 1);
-    __syncthreads();
-  }
-  {
-    const int last = FULL ? TPW - 1 : n_tiles - 1;
-    if (last >= 0) store(last);
   }
   if (a.n_exact && n_exact) atomicAdd(a.n_exact, n_exact);
 }
 
 template <int FMT, int TPW>
 __global__ __launch_bounds__(kQWaves * 64) void quant_kernel(QuantArgs a) {
-  __shared__ __attribute__((aligned(16))) QuantLds L;
+  __shared__ __attribute__((aligned(16))) QuantLds<TPW> L;
   int cg, tg;
   wg_coords(a.n_pg, a.n_tg, cg, tg);
-  const bool full = ((int64_t)(tg + 1) * TPW * 32 <= a.M) && (a.K % (kPanels * 32) == 0);
+  const bool full = ((int64_t)(tg + 1) * TPW * 32 <= a.M) && (a.K % (kPanels * 32) == 0) && a.K <= (1 << 26);
   if (full) quant_run<FMT, TPW, true>(a, L, cg, tg);
   else quant_run<FMT, TPW, false>(a, L, cg, tg);
 }
@@ -727,7 +710,6 @@ static hipError_t launch_quant_fmt(const QuantArgs& a, int n_wg, hipStream_t s) 
     case 1: hipLaunchKernelGGL((quant_kernel<FMT, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((quant_kernel<FMT, 2>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((quant_kernel<FMT, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((quant_kernel<FMT, 8>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
