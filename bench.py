@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: > 2x MALL)")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the hot-cache and device-copy context runs (for counter profiles)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the path, run a plain device copy of this many MiB --steps times "
@@ -212,6 +214,23 @@ def cpu_baseline(wl, x_bits_np, t_bits_np, seconds: float):
     }
 
 
+def context_runs(graph_ms, launch, sets, n_sets, nbytes, M, K, dev):
+    """The kernel on one buffer set (inputs served from the Infinity Cache),
+    and a plain device copy moving the same bytes, cold.  The copy moves the
+    activation bytes themselves (the first half of each set's X), since
+    bandwidth on this part depends on the data."""
+    import torch
+
+    hot_ms = graph_ms(lambda i: launch(0), 64, 4)
+    half = min(nbytes // 2, M * K * 2) // 16 * 16
+    csets = [(X.view(torch.uint8).view(-1)[:half], torch.empty(half, dtype=torch.uint8, device=dev))
+             for X, _, _, _ in sets]
+    copy_ms = graph_ms(lambda i: csets[i % n_sets][1].copy_(csets[i % n_sets][0]), n_sets * 4, 4)
+    del csets
+    torch.cuda.synchronize()
+    return hot_ms, copy_ms
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -293,31 +312,25 @@ def main():
     torch.cuda.synchronize()
     kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
 
-    # Timed region: exactly K steps back to back.  In graph mode the steps
-    # are replayed from HIP graphs (one rotation over the buffer sets per
-    # graph), so host launch cost does not gate the device.
-    graphs = []
+    # Timed region: exactly K steps back to back.  In graph mode the K steps
+    # are one HIP graph (each launch on the next buffer set), so neither host
+    # launch cost nor graph-to-graph gaps gate the device.
     if args.mode == "graph":
         cap = torch.cuda.Stream()
-        full, rem = divmod(args.steps, n_sets)
 
-        def capture(n):
+        def capture(n, first=0):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
-                for i in range(n):
+                for i in range(first, first + n):
                     launch(i)
             return g
 
-        g_full = capture(n_sets) if full else None
-        g_rem = capture(rem) if rem else None
-        # one untimed replay of each graph uploads it (not counted as a step)
-        for g in (g_full, g_rem):
-            if g is not None:
-                g.replay()
+        g_timed = capture(args.steps)
+        g_timed.replay()  # uploads the graph; not counted as steps
         torch.cuda.synchronize()
     # Warmup: W untimed steps, directly before the timed region.
     if args.mode == "graph" and args.warmup:
-        wg = capture(args.warmup)
+        wg = capture(args.warmup, args.steps)
         wg.replay()
     else:
         for i in range(args.warmup):
@@ -327,10 +340,7 @@ def main():
     wall0 = time.perf_counter()
     t_start.record()
     if args.mode == "graph":
-        for _ in range(full):
-            g_full.replay()
-        if g_rem is not None:
-            g_rem.replay()
+        g_timed.replay()
     else:
         for i in range(args.steps):
             launch(i)
@@ -350,9 +360,7 @@ def main():
     kern_avg_ms = ms_per_step
     achieved = nbytes / (kern_avg_ms * 1e-3) / 1e9
 
-    # Context, not the metric: the same kernel on one buffer set (inputs
-    # served from the Infinity Cache), and a plain device copy moving the
-    # same number of bytes, cold, as the achievable streaming reference.
+    # Context, not the metric: hot caches and a plain device copy.
     def graph_ms(fn, n, reps):
         cap = torch.cuda.Stream()
         g = torch.cuda.CUDAGraph()
@@ -369,15 +377,9 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (n * reps)
 
-    hot_ms = graph_ms(lambda i: launch(0), 64, 4)
-    # The copy moves the activation bytes themselves (the first half of each
-    # set's X), since bandwidth on this part depends on the data.
-    half = min(nbytes // 2, M * K * 2) // 16 * 16
-    csets = [(X.view(torch.uint8).view(-1)[:half], torch.empty(half, dtype=torch.uint8, device=dev))
-             for X, _, _, _ in sets]
-    copy_ms = graph_ms(lambda i: csets[i % n_sets][1].copy_(csets[i % n_sets][0]), n_sets * 4, 4)
-    del csets
-    torch.cuda.synchronize()
+    hot_ms = copy_ms = float("nan")
+    if not args.no_context:
+        hot_ms, copy_ms = context_runs(graph_ms, launch, sets, n_sets, nbytes, M, K, dev)
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name)
@@ -429,7 +431,8 @@ def main():
                                             round(float(np.percentile(kern_ms, 90)) * 1e3, 3)],
         },
     }
-    out["context"] = {
+    half = min(nbytes // 2, M * K * 2) // 16 * 16
+    out["context"] = None if args.no_context else {
         "hot_cache_us_per_step": round(hot_ms * 1e3, 3),
         "hot_cache_GBps": round(nbytes / (hot_ms * 1e-3) / 1e9, 2),
         "device_copy_cold": {"bytes_read_plus_written": 2 * half, "us": round(copy_ms * 1e3, 3),

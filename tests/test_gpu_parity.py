@@ -92,19 +92,24 @@ def test_tiny_workload(fmt):
     print(fmt, rep)
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
-@pytest.mark.parametrize("M,K", [(1, 32), (31, 64), (33, 256), (100, 96), (257, 160), (64, 48)])
+# Shapes that leave partial tiles in M, partial 256-channel columns in K, or
+# both, and launches that mix complete and partial workgroups (M past a
+# multiple of 64, K a multiple of 256 plus a remainder).
+_RAGGED = [(1, 32), (31, 64), (33, 256), (100, 96), (257, 160), (70, 256), (100, 512), (1000, 768),
+           (96, 288), (130, 4096 + 32)]
+_RAGGED_G16 = [(64, 48), (40, 272), (65, 16)]
+
+
+@pytest.mark.parametrize("fmt,M,K", [(f, M, K) for f in ("mxfp4", "nvfp4", "int4") for M, K in _RAGGED] +
+                         [("nvfp4", M, K) for M, K in _RAGGED_G16])
 def test_ragged_shapes(fmt, M, K):
     G = 16 if fmt == "nvfp4" else 32
-    if K % G:
-        pytest.skip("K not a multiple of G")
-    if fmt != "nvfp4" and K % 32:
-        pytest.skip("K must be a multiple of 32")
+    assert K % G == 0
     rng = np.random.default_rng(M * 1000 + K)
     X = rng.standard_t(3, (M, K))
     X[:, rng.choice(K, max(1, K // 64), replace=False)] *= 30
-    W = rng.standard_normal((2 * K, K)) * 0.02
-    Xc = rng.standard_t(3, (4 * K, K))
+    W = rng.standard_normal((min(2 * K, 512), K)) * 0.02
+    Xc = rng.standard_t(3, (min(4 * K, 1024), K))
     T64, _ = tr.build_transforms(W, Xc, G)
     xb, tb = f64_to_bf16_bits(X), tr.transforms_to_bf16_bits(T64)
     g = _g_for(xb, tb) if fmt == "nvfp4" else None
@@ -200,6 +205,29 @@ def test_full_size_sampled_rows(name):
     c, s, n = _run(wl.fmt, xb, tb, g, n_exact=True)
     rep = parity.check(wl.fmt, xb[rows], tb, c[rows], s[rows], g)
     print(name, rep, "exact groups:", n, "of", wl.M * wl.C, flush=True)
+
+
+# Batches big enough that workgroups take runs of 2 or 4 tiles, with a
+# ragged last run: M = 4100 at K = 4096 (two-tile runs, the last run one
+# partial tile) and M = 4136 at K = 8192 (four-tile runs, the last run two
+# tiles, the second partial).  The oracle checks sampled rows, which
+# include every row of the last two tiles.
+@pytest.mark.parametrize("fmt,M,K", [("mxfp4", 4100, 4096), ("int4", 4136, 8192), ("nvfp4", 4100, 4096)])
+def test_long_runs_with_ragged_tail(fmt, M, K):
+    print("case", fmt, M, K, flush=True)
+    G = 16 if fmt == "nvfp4" else 32
+    rng = np.random.default_rng(M + K)
+    X = rng.laplace(0.0, 1.0, (M, K))
+    X[:, rng.choice(K, K // 100, replace=False)] *= 50
+    W = rng.standard_normal((256, K)) * 0.02
+    Xc = rng.laplace(0.0, 1.0, (512, K))
+    T64, _ = tr.build_transforms(W, Xc, G)
+    xb, tb = f64_to_bf16_bits(X), tr.transforms_to_bf16_bits(T64)
+    rows = np.union1d(cases.sample_rows(M, n_edge=16, n_rand=48), np.arange(M - 64, M))
+    g = _g_for(xb, tb) if fmt == "nvfp4" else None
+    c, s = _run(fmt, xb, tb, g)
+    rep = parity.check(fmt, xb[rows], tb, c[rows], s[rows], g)
+    print(fmt, M, K, rep, flush=True)
 
 
 # ---------------------------------------------------------------- support entry points
