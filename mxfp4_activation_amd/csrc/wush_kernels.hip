@@ -224,6 +224,11 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // statement, so the compiler cannot hoist this rare path's float64
 // conversions of T out of the hot loop into registers that stay live.
 __device__ __forceinline__ void exact_panel(int n, const Frag& f, const XTile& x, f32x16& acc, float* lds, int lane) {
+  // Addresses below derive from an opaque copy of the lane id, so the
+  // compiler keeps their arithmetic inside this rarely taken path.
+  int lds_off = 0;
+  asm volatile("" : "+v"(lane), "+v"(lds_off));
+  lds += lds_off;
   const int i = lane & 31, h = lane >> 5;
   const int row = permuted_row(i);
   u32x4 tk[2] = {f.t0, f.t1};
@@ -259,7 +264,8 @@ __device__ __forceinline__ void exact_panel(int n, const Frag& f, const XTile& x
 // 16 values -> 16 E2M1 codes in two words, value r in nibble r.  `scale` is
 // applied by the conversion as a division by 2^(its exponent field).
 __device__ __forceinline__ u32x2 pack_e2m1(const f32x16& v, float scale) {
-  uint32_t w0 = 0u, w1 = 0u;
+  // Each word's four bytes are all written below, so any initial value works.
+  uint32_t w0 = __float_as_uint(scale), w1 = w0;
   w0 = cvt_e2m1x2<0>(w0, v[0], v[1], scale);
   w0 = cvt_e2m1x2<1>(w0, v[2], v[3], scale);
   w0 = cvt_e2m1x2<2>(w0, v[4], v[5], scale);
@@ -303,13 +309,14 @@ __device__ __forceinline__ u32x2 pack_int4(const f32x16& v, float r) {
 }
 
 // Bound on |fp32 MFMA result - exact sum| for a group whose |T||x| sums
-// peak at amax_abs.  The accumulation has at most 63 roundings of partial
-// sums bounded by amax_abs, each below 2^-23 relative (truncation is the
-// worst case), so 2^-17 covers it.  A term of 2^-21 * amax covers the final
-// rounding of y to fp32.  2^-120 covers products flushed at the bottom of
-// the fp32 range.
-__device__ __forceinline__ float err_bound(float amax_abs, float amax) {
-  return __builtin_fmaf(0x1p-17f, amax_abs, __builtin_fmaf(0x1p-21f, amax, 0x1p-120f));
+// peak at bound * bound_scale * 2^17.  The accumulation has at most 63
+// roundings of partial sums bounded by that peak, each below 2^-23 relative
+// (truncation is the worst case), so 2^-17 of the peak covers it; the
+// caller folds 2^-17 into bound_scale.  A term of 2^-21 * amax covers the
+// final rounding of y to fp32.  2^-120 covers products flushed at the
+// bottom of the fp32 range.
+__device__ __forceinline__ float err_bound(float bound, float bound_scale, float amax) {
+  return __builtin_fmaf(bound, bound_scale, __builtin_fmaf(0x1p-21f, amax, 0x1p-120f));
 }
 
 // Workgroup -> (panel group, token group).  Workgroups are dispatched
@@ -332,13 +339,13 @@ __device__ __forceinline__ void wg_coords(int n_pg, int n_tg, int& pg, int& tg) 
 // Groups whose scale decision falls within the accumulation error bound of
 // a boundary are recomputed exactly first.
 template <int FMT>
-__device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, const Frag& f,
+__device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float bound_scale, const Frag& f,
                                                 const XTile& x, float g, float* lds, int lane,
                                                 uint32_t& scale_bits, uint32_t& n_exact) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   float amax = max_abs16(acc);
   if (G == 32) amax = max_halves(amax);
-  const float d = err_bound(bound, amax);
+  const float d = err_bound(bound, bound_scale, amax);
   bool unsure;
   if (FMT == kMXFP4) {
     // The E8M0 code depends only on the exponent field of amax.  It is
@@ -355,7 +362,7 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, const 
       int ln = __builtin_ctzll(pending) & 31;
       exact_panel(ln, f, x, acc, lds, lane);
       pending &= ~((1ull << ln) | (1ull << (ln + 32)));
-      n_exact += (lane == 0) ? 1u : 0u;
+      ++n_exact;  // wave-uniform count
     }
     amax = max_abs16(acc);
     if (G == 32) amax = max_halves(amax);
@@ -388,25 +395,35 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, const 
   }
 }
 
-// Largest |T| entry of the panel held by this wave, as a float.
+// max(v, v of the lane that DPP control CTRL selects), for non-negative v.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+  return v > o ? v : o;
+}
+
+// Largest |T| entry of the panel held by this wave, as a float (uniform).
+// Non-negative bf16 values order like their 16-bit patterns, so the
+// in-lane part is a packed 16-bit max.  Across lanes: quad swaps, half-row
+// and row mirrors give every lane its 16-lane row maximum, then the four
+// rows are read out to scalar registers.
 __device__ __forceinline__ float panel_tmax(const Frag& f) {
-  uint32_t m = 0;
-  const u32x4 w[2] = {f.t0, f.t1};
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t mask = 0x7FFF7FFFu;
+  u16x2 m = __builtin_bit_cast(u16x2, f.t0[0] & mask);
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int e = 1; e < 4; ++e) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, f.t0[e] & mask));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t lo = w[k][e] & 0x7FFFu, hi = (w[k][e] >> 16) & 0x7FFFu;
-      m = m > lo ? m : lo;
-      m = m > hi ? m : hi;
-    }
-  }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t v = (uint32_t)__shfl_xor((int)m, o, 64);
-    m = m > v ? m : v;
-  }
-  return __uint_as_float(m << 16);
+  for (int e = 0; e < 4; ++e) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, f.t1[e] & mask));
+  uint32_t r = m.x > m.y ? m.x : m.y;
+  r = dpp_max<0xB1>(r);   // quad_perm [1,0,3,2]
+  r = dpp_max<0x4E>(r);   // quad_perm [2,3,0,1]
+  r = dpp_max<0x141>(r);  // row_half_mirror
+  r = dpp_max<0x140>(r);  // row_mirror
+  const uint32_t a = __builtin_amdgcn_readlane(r, 0), b = __builtin_amdgcn_readlane(r, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(r, 32), d = __builtin_amdgcn_readlane(r, 48);
+  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return __uint_as_float((ab > cd ? ab : cd) << 16);
 }
 
 }  // namespace
@@ -449,21 +466,21 @@ struct QuantLds {
 };
 
 // Contract and quantize panel `wave` of one staged tile; write its codes and
-// scales back into the tile.
+// scales back into the tile.  `row` is this lane's row of the tile.
 //
 // The accumulation bound: for MXFP4, whose scale boundaries are powers of
-// two, the cheap bound tmax * sum_j |x_j| suffices.  Its MFMA has every row
-// of A equal to one, so every output row holds the token's L1 norm.  INT4
-// and NVFP4 scales have much denser boundaries, so they use the per-output
-// bound max_k sum_j |T_kj x_j| from an |T| x |x| MFMA.
+// two, the cheap bound max|T| * sum_j |x_j| suffices.  Its MFMA has every
+// row of A equal to one (`ones`), so every output row holds the token's L1
+// norm; bscale is max|T| * 2^-17.  INT4 and NVFP4 scales have much denser
+// boundaries, so they use the per-output bound max_k sum_j |T_kj x_j| from
+// an |T| x |x| MFMA, with bscale = 2^-17.
 template <int FMT>
-__device__ __forceinline__ void panel_step(uint8_t* xs, float* ybuf, const Frag& f, float tmax, float g, int wave,
-                                           int lane, uint32_t& n_exact) {
+__device__ __forceinline__ void panel_step(uint8_t* row, float* ybuf, const Frag& f, const u32x4& ones, float bscale,
+                                           float g, int wave, int lane, uint32_t& n_exact) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
-  const int n = lane & 31, h = lane >> 5;
+  const int h = lane >> 5;
   const u32x4 mask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
   XTile x;
-  uint8_t* row = xs + n * kXRow;
   x.b0 = *reinterpret_cast<const u32x4*>(row + wave * 64 + 16 * h);
   x.b1 = *reinterpret_cast<const u32x4*>(row + wave * 64 + 16 * h + 32);
   f32x16 zero = {};
@@ -471,10 +488,9 @@ __device__ __forceinline__ void panel_step(uint8_t* xs, float* ybuf, const Frag&
   acc = mfma32(f.t1, x.b1, acc);
   float bound;
   if (FMT == kMXFP4) {
-    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
     f32x16 l1 = mfma32(ones, x.b0 & mask, zero);
     l1 = mfma32(ones, x.b1 & mask, l1);
-    bound = tmax * l1[0];
+    bound = l1[0];
   } else {
     f32x16 aab = mfma32(f.t0 & mask, x.b0 & mask, zero);
     aab = mfma32(f.t1 & mask, x.b1 & mask, aab);
@@ -482,7 +498,7 @@ __device__ __forceinline__ void panel_step(uint8_t* xs, float* ybuf, const Frag&
     if (G == 32) bound = max_halves(bound);
   }
   uint32_t sbits;
-  const u32x2 w = quantize_panel<FMT>(acc, bound, f, x, g, ybuf, lane, sbits, n_exact);
+  const u32x2 w = quantize_panel<FMT>(acc, bound, bscale, f, x, g, ybuf, lane, sbits, n_exact);
   // Every lane of the wave has read its operands before any lane writes:
   // the reads above feed the MFMAs whose results the writes depend on.
   *reinterpret_cast<u32x2*>(row + wave * 64 + 8 * h) = w;
@@ -542,7 +558,9 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
       }
     }
   }
-  const float tmax = (FMT == kMXFP4) ? panel_tmax(f) : 0.0f;
+  const float bscale = (FMT == kMXFP4) ? panel_tmax(f) * 0x1p-17f : 0x1p-17f;
+  u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+  asm volatile("" : "+v"(ones));  // materialized once, kept in VGPRs
   float g = 0.0f;
   if (FMT == kNVFP4) g = *a.global_scale;
 
@@ -557,10 +575,11 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
   // 3. contract and quantize
   uint32_t n_exact = 0;
   if (panel_ok) {
+    uint8_t* row = L.xs[0] + (lane & 31) * kXRow;  // this lane's row; tiles at constant offsets
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       if (!FULL && u >= n_tiles) break;
-      panel_step<FMT>(L.xs[u], L.y[wave], f, tmax, g, wave, lane, n_exact);
+      panel_step<FMT>(row + u * (32 * kXRow), L.y[wave], f, ones, bscale, g, wave, lane, n_exact);
     }
   }
   __syncthreads();
@@ -618,11 +637,13 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
       }
     }
   }
-  if (a.n_exact && n_exact) atomicAdd(a.n_exact, n_exact);
+  if (a.n_exact && n_exact && lane == 0) atomicAdd(a.n_exact, n_exact);
 }
 
+// MXFP4 asks for 8 waves per SIMD (64 VGPRs): with 35 KB of LDS per
+// two-tile workgroup, four workgroups then share a CU.
 template <int FMT, int TPW>
-__global__ __launch_bounds__(kQWaves * 64) void quant_kernel(QuantArgs a) {
+__global__ __launch_bounds__(kQWaves * 64, (FMT == kMXFP4) ? 8 : 1) void quant_kernel(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) QuantLds<TPW> L;
   int cg, tg;
   wg_coords(a.n_pg, a.n_tg, cg, tg);
