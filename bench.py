@@ -37,6 +37,30 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MALL_BYTES = 256 << 20
 
 
+TRANSFORMS = ("wush", "wus", "hadamard", "identity")
+
+
+def build_bank(name, wl):
+    """bf16 transform bank [C][G][G] for a workload.  WUSH and WUS come from
+    the workload's weight and calibration statistics (product builder);
+    the blockwise Hadamard and the identity are the pages' data-agnostic
+    comparators (RTN-H and plain RTN)."""
+    import torch
+
+    from mxfp4_activation_amd import transforms
+    from synthetic import gen_calibration, gen_weight
+
+    C, G = wl.K // wl.G, wl.G
+    if name in ("wush", "wus"):
+        T, _ = transforms.wush_transforms(torch.from_numpy(gen_weight(wl)), torch.from_numpy(gen_calibration(wl)), G,
+                                          use_hadamard=(name == "wush"))
+    elif name == "hadamard":
+        T = transforms.hadamard_transforms(C, G)
+    else:
+        T = transforms.identity_transforms(C, G)
+    return transforms.to_kernel_layout(T)
+
+
 def algorithmic_bytes(fmt: str, M: int, K: int, G: int) -> int:
     scale_bytes = 2 if fmt == "int4" else 1
     return M * K * 2 + M * K // 2 + M * (K // G) * scale_bytes + (K // G) * G * G * 2
@@ -58,6 +82,12 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the path, run a plain device copy of this many MiB --steps times "
                          "(reference for the HBM byte counters)")
+    ap.add_argument("--transform", choices=list(TRANSFORMS), default="wush",
+                    help="transform bank fed to the same kernel: wush (default), wus (no Hadamard), "
+                         "hadamard (blockwise H, the RTN-H comparator), identity (plain RTN)")
+    ap.add_argument("--compare-transforms", action="store_true",
+                    help="instead of the step benchmark, time all transform banks through the same kernel, "
+                         "interleaved in one process, and print one JSON line")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="instead of running, read four rocprofv3 --pmc output folders (FETCH_SIZE and "
                          "WRITE_SIZE of the path, then of --copy-probe-mib) and write "
@@ -231,6 +261,87 @@ def context_runs(graph_ms, launch, sets, n_sets, nbytes, M, K, dev):
     return hot_ms, copy_ms
 
 
+def compare_transforms(args) -> None:
+    """WUSH against the comparators through the same kernel: the same cold
+    rotating buffer sets, one HIP graph per transform, replays interleaved
+    so drift affects all alike; median over repetitions."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import mxfp4_activation_amd as wush
+    from mxfp4_activation_amd import _lib
+    from synthetic import CONFIGS, gen_x_bits
+
+    wl = CONFIGS[args.workload]
+    M, K, G, fmt = wl.M, wl.K, wl.G, wl.fmt
+    lib = wush.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    X0 = torch.from_numpy(gen_x_bits(wl).view(np.int16)).view(torch.bfloat16).to(dev)
+    banks = {name: build_bank(name, wl).to(dev) for name in TRANSFORMS}
+    nbytes = algorithmic_bytes(fmt, M, K, G)
+    n_sets = args.sets or max(2, -(-2 * MALL_BYTES // nbytes) + 1)
+    sdt = torch.float16 if fmt == "int4" else torch.uint8
+    xs = [X0.clone() if i else X0 for i in range(n_sets)]
+    outs = [(torch.empty((M, K // 2), dtype=torch.uint8, device=dev), torch.empty((M, K // G), dtype=sdt, device=dev))
+            for _ in range(n_sets)]
+    tsets = {name: [T.clone() for _ in range(n_sets)] for name, T in banks.items()}
+    gscale = torch.zeros(1, dtype=torch.float32, device=dev)
+    counts = torch.zeros(len(TRANSFORMS), dtype=torch.int32, device=dev)
+    fmt_id = _lib.FMT[fmt]
+    cap = torch.cuda.Stream()
+    graphs = {}
+    for ti, name in enumerate(TRANSFORMS):
+        if fmt == "nvfp4":
+            g = torch.zeros(1, dtype=torch.float32, device=dev)
+            wush.nvfp4_global_scale(X0, banks[name], out=g)
+        else:
+            g = gscale
+
+        def launch(i, name=name, g=g, cnt=None):
+            c, s = outs[i % n_sets]
+            st = lib.wush_quant(fmt_id, xs[i % n_sets].data_ptr(), tsets[name][i % n_sets].data_ptr(), M, K,
+                                g.data_ptr() if fmt == "nvfp4" else None, c.data_ptr(), s.data_ptr(),
+                                None if cnt is None else cnt, torch.cuda.current_stream().cuda_stream)
+            if st:
+                _lib.check(st, "wush_quant")
+
+        launch(0, cnt=counts[ti:ti + 1].data_ptr())  # exact recomputations of one launch
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=cap):
+            for i in range(n_sets * 4):
+                launch(i)
+        gr.replay()
+        graphs[name] = gr
+    torch.cuda.synchronize()
+    times = {name: [] for name in TRANSFORMS}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(max(3, args.steps // 40)):
+        for name in TRANSFORMS:
+            torch.cuda.synchronize()
+            e0.record()
+            graphs[name].replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times[name].append(e0.elapsed_time(e1) * 1e3 / (n_sets * 4))
+    cnt = counts.cpu().tolist()
+    res = {}
+    for ti, name in enumerate(TRANSFORMS):
+        us = statistics.median(times[name])
+        res[name] = {"us_per_step": round(us, 3), "GBps": round(nbytes / us / 1e3, 2),
+                     "exact_groups_per_launch": cnt[ti]}
+    gap = 100.0 * (res["wush"]["us_per_step"] / res["hadamard"]["us_per_step"] - 1.0)
+    print(json.dumps({
+        "comparison": "transform banks through the same fused kernel (cold, interleaved graphs, median)",
+        "workload": wl.name, "format": fmt, "tokens": M, "d": K, "G": G,
+        "algorithmic_bytes_per_step": nbytes, "results": res,
+        "wush_vs_hadamard_time_pct": round(gap, 2),
+        "pages": "WUSH+Quant within about 1.3% of H+Quant on average (papernotes results; deep dive 3.4.7, 5)",
+    }), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -245,6 +356,9 @@ def main():
         return
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, args.steps)
+        return
+    if args.compare_transforms:
+        compare_transforms(args)
         return
 
     import numpy as np
@@ -263,8 +377,7 @@ def main():
 
     # Inputs: seeded activations and the offline transform bank.
     x_np = gen_x_bits(wl)
-    Tw, _ = transforms.wush_transforms(torch.from_numpy(gen_weight(wl)), torch.from_numpy(gen_calibration(wl)), G)
-    T_bf16 = transforms.to_kernel_layout(Tw)
+    T_bf16 = build_bank(args.transform, wl)
     t_np = T_bf16.view(torch.int16).numpy().view(np.uint16)
     X0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
     T0 = T_bf16.to(dev)
@@ -407,6 +520,7 @@ def main():
                         "W [%d x %d] N(0,0.02) and %d calibration tokens" % (
                             wl.name, M, K, G, wl.dist, wl.n_outlier, wl.outlier_mult, wl.d_out, K, wl.n_cal),
             "format": fmt,
+            "transform": args.transform,
             "tokens": M,
             "d": K,
             "G": G,

@@ -10,7 +10,7 @@ import pytest
 
 from oracle import codecs, quant
 from oracle import transform as tr
-from synthetic import CONFIGS, f64_to_bf16_bits
+from synthetic import CONFIGS, f64_to_bf16_bits, gen_calibration, gen_weight
 
 from . import cases, parity
 
@@ -131,7 +131,11 @@ def test_empty_batch_is_noop():
 # ---------------------------------------------------------------- special transforms
 
 
-@pytest.mark.parametrize("which", ["identity", "hadamard", "cyclic"])
+# The pages' comparators go through the same kernel (deep dive, section 5):
+# identity (plain RTN), blockwise Hadamard (RTN-H), and WUS (WUSH with the
+# Hadamard factor replaced by the identity).  A cyclic shift catches a
+# transposed T.
+@pytest.mark.parametrize("which", ["identity", "hadamard", "wus", "cyclic"])
 def test_special_transforms(which):
     wl = CONFIGS["tiny_mxfp4"]
     G, C = 32, wl.C
@@ -139,6 +143,8 @@ def test_special_transforms(which):
         T = np.broadcast_to(np.eye(G), (C, G, G))
     elif which == "hadamard":
         T = np.broadcast_to(tr.hadamard(G), (C, G, G))
+    elif which == "wus":
+        T, _ = tr.build_transforms(gen_weight(wl), gen_calibration(wl), G, H=np.eye(G))
     else:
         T = np.zeros((C, G, G))
         for c in range(C):
