@@ -469,9 +469,8 @@ struct QuantLds {
 // scales back into the tile.  `row` is this lane's row of the tile.
 //
 // The accumulation bound: for MXFP4, whose scale boundaries are powers of
-// two, the cheap bound max|T| * sum_j |x_j| suffices.  Its MFMA has every
-// row of A equal to one (`ones`), so every output row holds the token's L1
-// norm; bscale is max|T| * 2^-17.  INT4 and NVFP4 scales have much denser
+// two, a cheap bound max|T| * (L1 norm) suffices; an all-ones MFMA gives the
+// L1 norms (of a token pair, see below); bscale is max|T| * 2^-17.  INT4 and NVFP4 scales have much denser
 // boundaries, so they use the per-output bound max_k sum_j |T_kj x_j| from
 // an |T| x |x| MFMA, with bscale = 2^-17.
 template <int FMT>
@@ -488,8 +487,18 @@ __device__ __forceinline__ void panel_step(uint8_t* row, float* ybuf, const Frag
   acc = mfma32(f.t1, x.b1, acc);
   float bound;
   if (FMT == kMXFP4) {
-    f32x16 l1 = mfma32(ones, x.b0 & mask, zero);
-    l1 = mfma32(ones, x.b1 & mask, l1);
+    // v_mfma_f32_16x16x32_bf16 on the same operand registers, at half the
+    // cost of the 32x32x16 pair.  In its B layout, lane l supplies 8 values
+    // of column l % 16 for k-slot l / 16, so column n sums |x| over lanes
+    // n, n + 16, n + 32, n + 48: 16 channels of tokens n and n + 16.  With
+    // both k-slices accumulated, every output of column n is
+    // |x_n|_1 + |x_(n+16)|_1, an upper bound on token n's L1 norm (and on
+    // token n + 16's), and lane l reads column l % 16.
+    f32x4 z4 = {};
+    f32x4 l1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones),
+                                                       __builtin_bit_cast(bf16x8, x.b0 & mask), z4, 0, 0, 0);
+    l1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones),
+                                                 __builtin_bit_cast(bf16x8, x.b1 & mask), l1, 0, 0, 0);
     bound = l1[0];
   } else {
     f32x16 aab = mfma32(f.t0 & mask, x.b0 & mask, zero);
