@@ -94,7 +94,7 @@ void plan_quant(int64_t M, int64_t K, int64_t* n_tiles, int64_t* tpw, int* n_pan
   *n_tiles = (M + 31) / 32;
   *n_panels = (int)((K + 31) / 32);
   *n_pg = (*n_panels + wush::kPanelsPerTile - 1) / wush::kPanelsPerTile;
-  const int64_t target_wg = 1024;
+  const int64_t target_wg = 8192 / wush::kPanelsPerTile;  // 4 eight-wave workgroups per CU
   int64_t t = 4;
   while (t > 1 && (int64_t)(*n_pg) * ((*n_tiles + t - 1) / t) < target_wg) t >>= 1;
   static const int64_t env = [] {

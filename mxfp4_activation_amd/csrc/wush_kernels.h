@@ -14,7 +14,10 @@ constexpr int kNVFP4 = 1;
 constexpr int kINT4 = 2;
 
 constexpr int kWavesPerGroup = 4;   // waves per workgroup
-constexpr int kPanelsPerTile = 8;   // quant kernel: 32-channel panels per workgroup tile
+#ifndef WUSH_QUANT_PANELS
+#define WUSH_QUANT_PANELS 8
+#endif
+constexpr int kPanelsPerTile = WUSH_QUANT_PANELS;  // quant kernel: 32-channel panels (= waves) per workgroup
 
 struct QuantArgs {
   const uint16_t* X;

@@ -453,10 +453,11 @@ __device__ __forceinline__ float panel_tmax(const Frag& f) {
 // Rows past M are loaded from row M-1 and not stored.  Channels past K
 // are not loaded; they are zero in LDS, and T is zero there too.
 
-constexpr int kQWaves = 8;            // waves per quant workgroup (one panel each)
-constexpr int kPanels = kQWaves;      // panels (32 channels each) per tile
-constexpr int kXRow = 512 + 16;       // LDS bytes per row: 256 bf16, then 16 B of scales
-constexpr int kScaleOff = 512;        // scales of a row start here
+constexpr int kQWaves = kPanelsPerTile;  // waves per quant workgroup (one panel each)
+constexpr int kPanels = kQWaves;         // panels (32 channels each) per tile
+constexpr int kChunks = 4 * kPanels;     // 16-byte chunks per tile row
+constexpr int kScaleOff = kPanels * 64;  // scales of a row start here
+constexpr int kXRow = kScaleOff + 16;    // LDS bytes per row: the channels, then 16 B of scales
 
 // LDS of one quant workgroup.
 template <int TPW>
@@ -547,8 +548,8 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
     f = panel_ok ? load_t<G>(a.T, p0 + wave, C, lane) : Frag{z, z, z, z};
   }
   // Thread t covers 16-byte chunk t%32 of rows t/32 and t/32 + 16 of each tile.
-  const int chunk = tid & 31;
-  const int row_a = tid >> 5;
+  const int chunk = tid % kChunks;
+  const int row_a = tid / kChunks;  // 0..15
   const int64_t ch0 = (int64_t)p0 * 32 + 8 * chunk;
   const bool chunk_ok = FULL || ch0 < K;
   u32x4 v[TPW][2];
@@ -593,36 +594,41 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
   }
   __syncthreads();
 
-  // 4. whole-row stores: thread t < 256 stores 16 B of codes (row t/8,
-  // panel t%8), threads 256..287 store one row's scales.
+  // 4. whole-row stores: thread t < 32 * kPanels stores 16 B of codes
+  // (row t / kPanels, panel t % kPanels); the next 32 threads store one
+  // row's scales each.
   const int s_elem = (FMT == kINT4) ? 2 : 1;
   const int64_t s_first = (G == 32) ? p0 : 2 * p0;  // first scale index of the tile in a row
   const int s_max = (G == 32) ? kPanels : 2 * kPanels;
   const int s_count = FULL ? s_max : (int)(((int64_t)C - s_first) < s_max ? (int64_t)C - s_first : s_max);
   const int64_t code_bytes_left = K / 2 - (int64_t)p0 * 16;
   const int code_row_bytes = FULL ? kPanels * 16 : (int)(code_bytes_left < kPanels * 16 ? code_bytes_left : kPanels * 16);
-  const int c_row = (tid & 255) >> 3, c_panel = tid & 7;
+  constexpr int kCodeThreads = 32 * kPanels;
+  const int c_row = tid / kPanels, c_panel = tid % kPanels;
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     if (!FULL && u >= n_tiles) break;
     const int64_t t = tile0 + u;
     const uint8_t* xs = L.xs[u];
     if (FULL) {
-      if (tid < 256) {
+      if (tid < kCodeThreads) {
         uint8_t* base = a.codes + (t * 32) * (K / 2) + (int64_t)p0 * 16;  // uniform
         const uint32_t off = (uint32_t)(c_row * (K / 2) + 16 * c_panel);
         *reinterpret_cast<u32x4*>(base + off) = *reinterpret_cast<const u32x4*>(xs + c_row * kXRow + 64 * c_panel);
-      } else if (tid < 288) {
-        const int r = tid - 256;
+      } else if (tid < kCodeThreads + 32) {
+        const int r = tid - kCodeThreads;
         uint8_t* base = a.scales + ((t * 32) * C + s_first) * s_elem;  // uniform
         const uint32_t off = (uint32_t)(r * C * s_elem);
-        if (s_max * s_elem == 8)
-          *reinterpret_cast<u32x2*>(base + off) = *reinterpret_cast<const u32x2*>(xs + r * kXRow + kScaleOff);
+        const uint8_t* src = xs + r * kXRow + kScaleOff;
+        if (s_max * s_elem == 4)
+          *reinterpret_cast<uint32_t*>(base + off) = *reinterpret_cast<const uint32_t*>(src);
+        else if (s_max * s_elem == 8)
+          *reinterpret_cast<u32x2*>(base + off) = *reinterpret_cast<const u32x2*>(src);
         else
-          *reinterpret_cast<u32x4*>(base + off) = *reinterpret_cast<const u32x4*>(xs + r * kXRow + kScaleOff);
+          *reinterpret_cast<u32x4*>(base + off) = *reinterpret_cast<const u32x4*>(src);
       }
     } else {
-      if (tid < 256) {
+      if (tid < kCodeThreads) {
         const int64_t m = t * 32 + c_row;
         if (m < M && 16 * c_panel < code_row_bytes) {
           uint8_t* dst = a.codes + m * (K / 2) + (int64_t)p0 * 16 + 16 * c_panel;
@@ -634,8 +640,8 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
             *reinterpret_cast<u32x2*>(dst) = h8;
           }
         }
-      } else if (tid < 288) {
-        const int r = tid - 256;
+      } else if (tid < kCodeThreads + 32) {
+        const int r = tid - kCodeThreads;
         const int64_t m = t * 32 + r;
         if (m < M) {
           uint8_t* dst = a.scales + (m * C + s_first) * s_elem;
