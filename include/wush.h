@@ -104,6 +104,28 @@ wush_status wush_quant(int fmt, const void* X, const void* T, int64_t M, int64_t
                        const float* global_scale, void* codes, void* scales,
                        uint32_t* n_exact, hipStream_t stream);
 
+/* Output element type of wush_gemm_mxfp4. */
+typedef enum { WUSH_OUT_F32 = 0, WUSH_OUT_BF16 = 1 } wush_out_type;
+
+/* MXFP4 GEMM: the FP4 matrix multiplication of the inference forward pass
+ * ("WUSH: Near-Optimal Adaptive Transforms for LLM Quantization", deep dive,
+ * section 3.4.6, Eq. 10).  With a and b the values that wush_quant_mxfp4
+ * encodes (E2M1 codes times the block's E8M0 scale),
+ *     C[m][n] = sum_k a[m][k] * b[n][k],
+ * accumulated in fp32 on the matrix cores.
+ *   a_codes:  u8 [M][K/2], a_scales: u8 [M][K/32]   (activations, e.g. the
+ *             quantized transform of a token batch)
+ *   b_codes:  u8 [N][K/2], b_scales: u8 [N][K/32]   (weights, quantized
+ *             offline with the weight-side transform)
+ *   C:        [M][N], fp32 or bf16 (round to nearest even), row-major.
+ * Requires K > 0 and K % 256 == 0; M, N >= 0 (0 is a no-op).  All pointers
+ * are device pointers owned by the caller; codes must be 16-byte aligned,
+ * scales 8-byte aligned, C 4-byte aligned, and C must not overlap an input.
+ * Errors as for wush_quant. */
+wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const void* b_codes,
+                            const void* b_scales, int64_t M, int64_t N, int64_t K, void* C,
+                            int out_type, hipStream_t stream);
+
 /* Transform only: Y[m][cG+i] = sum_j T[c][i][j] x_(cG+j), in fp32 from the
  * matrix cores, without rounding fix-up.  G is 16 or 32.  Use it to check
  * values before quantization, or when the transformed activations are wanted

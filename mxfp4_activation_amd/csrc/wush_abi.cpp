@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/wush.h"
+#include "wush_gemm.h"
 #include "wush_kernels.h"
 
 namespace {
@@ -257,6 +258,45 @@ wush_status wush_nvfp4_global_scale(const void* X, const void* T, int64_t M, int
   wush_status st = absmax_common(X, T, M, K, 16, global_scale, stream);
   if (st != WUSH_OK) return st;
   hipError_t e = wush::launch_global_scale(global_scale, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const void* b_codes,
+                            const void* b_scales, int64_t M, int64_t N, int64_t K, void* C, int out_type,
+                            hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (out_type != WUSH_OUT_F32 && out_type != WUSH_OUT_BF16) return fail(WUSH_EINVAL, "unknown out_type %d", out_type);
+  if (M < 0 || N < 0) return fail(WUSH_EINVAL, "M and N must be >= 0");
+  if (K <= 0 || K % 256 != 0) return fail(WUSH_EINVAL, "K must be a positive multiple of 256 (got %lld)", (long long)K);
+  if (K > ((int64_t)1 << 30)) return fail(WUSH_EINVAL, "K too large");
+  if (M == 0 || N == 0) return WUSH_OK;
+  if ((M + 127) / 128 > 65535) return fail(WUSH_EINVAL, "M too large for one launch");
+  if ((N + 127) / 128 > 0x7FFFFFFF) return fail(WUSH_EINVAL, "N too large for one launch");
+  if (M > (INT64_MAX / 8) / N || M > (INT64_MAX / 8) / K || N > (INT64_MAX / 8) / K)
+    return fail(WUSH_EINVAL, "sizes overflow");
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !C) return fail(WUSH_EINVAL, "null pointer");
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16)) return fail(WUSH_EALIGN, "codes must be 16-byte aligned");
+  if (!aligned(a_scales, 8) || !aligned(b_scales, 8)) return fail(WUSH_EALIGN, "scales must be 8-byte aligned");
+  if (!aligned(C, 4)) return fail(WUSH_EALIGN, "C must be 4-byte aligned");
+  const uint64_t nc = (uint64_t)M * N * (out_type == WUSH_OUT_F32 ? 4 : 2);
+  const uint64_t na = (uint64_t)M * K / 2, nb = (uint64_t)N * K / 2;
+  const uint64_t nsa = (uint64_t)M * K / 32, nsb = (uint64_t)N * K / 32;
+  if (overlap(C, nc, a_codes, na) || overlap(C, nc, b_codes, nb) || overlap(C, nc, a_scales, nsa) ||
+      overlap(C, nc, b_scales, nsb))
+    return fail(WUSH_EINVAL, "C overlaps an input");
+  wush_status st = check_device();
+  if (st != WUSH_OK) return st;
+  wush::GemmArgs g{};
+  g.a_codes = static_cast<const uint8_t*>(a_codes);
+  g.a_scales = static_cast<const uint8_t*>(a_scales);
+  g.b_codes = static_cast<const uint8_t*>(b_codes);
+  g.b_scales = static_cast<const uint8_t*>(b_scales);
+  g.C = C;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  hipError_t e = wush::launch_gemm_mxfp4(g, out_type == WUSH_OUT_BF16, stream);
   if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
   return WUSH_OK;
 }

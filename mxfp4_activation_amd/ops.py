@@ -79,6 +79,29 @@ def quant_int4(X, T, codes=None, scales=None):
     return quant("int4", X, T, codes=codes, scales=scales)
 
 
+def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
+               out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C[m][n] = sum_k a[m][k] b[n][k] for MXFP4 operands (codes [rows][K/2],
+    E8M0 scales [rows][K/32]), fp32 accumulation, output fp32 or bf16."""
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    for t in (a_codes, a_scales, b_codes, b_scales):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError("codes and scales must be contiguous 2-D uint8 device tensors")
+    M, N, K = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
+    if b_codes.shape[1] * 2 != K or tuple(a_scales.shape) != (M, K // 32) or tuple(b_scales.shape) != (N, K // 32):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    lib = _lib.load()
+    _lib.check(lib.wush_gemm_mxfp4(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(), b_scales.data_ptr(),
+                                   M, N, K, out.data_ptr(), 1 if out_dtype == torch.bfloat16 else 0, _stream()),
+               "wush_gemm_mxfp4")
+    return out
+
+
 def transform_f32(X: torch.Tensor, T: torch.Tensor, Y: Optional[torch.Tensor] = None) -> torch.Tensor:
     G = T.shape[-1]
     M, K = _check_x_t(X, T, G)

@@ -18,6 +18,9 @@ Quantization", arXiv 2512.00956):
   symmetric INT4 with an fp16 scale.  The pages name these formats but
   do not spell out their encodings.  The encodings here are the standard
   OCP MX / OCP FP8 / IEEE binary16 definitions.
+* ``gemm``       is the FP4 matrix product that consumes the quantized
+  activations and the pre-quantized weights (deep dive, section 3.4.6,
+  Eq. 10): decode both MXFP4 operands, multiply in float64.
 * ``quant``      is the online path.  For every token and block it computes
   y = T_wush(c) x.  Then it applies RTN AbsMax quantization of y in groups
   of G, the transform block (deep dive, sections 3.4.1 and 3.4.7; Eq. 10).

@@ -1,0 +1,44 @@
+"""Seeded random MXFP4 operands and the linear-layer shapes of the GEMM workload.
+
+Random bytes only: E2M1 code nibbles and E8M0 scale bytes drawn uniformly
+from the requested ranges.  Nothing here decodes or multiplies them.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, Tuple
+
+import numpy as np
+
+# Linear layers of one Qwen3-8B decoder block as (N = output features,
+# K = input features): hidden size 4096, 32 query heads and 8 key/value heads
+# of width 128, MLP width 12288.
+QWEN3_8B_LAYERS: Dict[str, Tuple[int, int]] = {
+    "q_proj": (4096, 4096),
+    "k_proj": (1024, 4096),
+    "v_proj": (1024, 4096),
+    "o_proj": (4096, 4096),
+    "gate_proj": (12288, 4096),
+    "up_proj": (12288, 4096),
+    "down_proj": (4096, 12288),
+}
+
+# Token batch of the per-layer GEMM measurement.
+GEMM_TOKENS = 1024
+
+
+def gen_mx_operand(rows: int, K: int, seed: int, scale_lo: int = 127, scale_hi: int = 127,
+                   mag_max: int = 7) -> Tuple[np.ndarray, np.ndarray]:
+    """(codes u8 [rows][K/2], scales u8 [rows][K/32]).
+
+    Each nibble has a uniform sign bit and a uniform magnitude code in
+    [0, mag_max]; each scale byte is uniform in [scale_lo, scale_hi]."""
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    rng = np.random.default_rng(seed)
+    mag = rng.integers(0, mag_max + 1, size=(rows, K), dtype=np.uint8)
+    sign = rng.integers(0, 2, size=(rows, K), dtype=np.uint8) << 3
+    nib = mag | sign
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales = rng.integers(scale_lo, scale_hi + 1, size=(rows, K // 32), dtype=np.uint8)
+    return codes, scales

@@ -77,3 +77,24 @@ def test_binding_raises_with_detail():
     st = lib.wush_quant_mxfp4(A, A, 8, 33, A * 2, A * 3, None)
     with pytest.raises(_lib.WushError, match="multiple of 32"):
         _lib.check(st, "wush_quant_mxfp4")
+
+
+def test_gemm_validation_rejects_bad_arguments():
+    lib = wush.load()
+    B = A * 64  # far apart: no overlaps unless a test places one
+    g = lambda ac, as_, bc, bs, M, N, K, C, t=0: lib.wush_gemm_mxfp4(ac, as_, bc, bs, M, N, K, C, t, None)
+    args = (A, A * 2, A * 3, A * 4)
+    assert g(*args, 0, 16, 256, B) == _lib.WUSH_OK  # M = 0: no-op
+    assert g(*args, 16, 0, 256, B) == _lib.WUSH_OK
+    assert g(*args, -1, 16, 256, B) == _lib.WUSH_EINVAL
+    assert g(*args, 16, 16, 128, B) == _lib.WUSH_EINVAL  # K not a multiple of 256
+    assert g(*args, 16, 16, 0, B) == _lib.WUSH_EINVAL
+    assert g(*args, 16, 16, 256, B, 2) == _lib.WUSH_EINVAL  # unknown output type
+    assert g(None, A * 2, A * 3, A * 4, 16, 16, 256, B) == _lib.WUSH_EINVAL
+    assert g(*args, 16, 16, 256, None) == _lib.WUSH_EINVAL
+    assert g(A + 8, A * 2, A * 3, A * 4, 16, 16, 256, B) == _lib.WUSH_EALIGN
+    assert g(A, A * 2 + 4, A * 3, A * 4, 16, 16, 256, B) == _lib.WUSH_EALIGN
+    assert g(*args, 16, 16, 256, B + 2) == _lib.WUSH_EALIGN
+    assert g(*args, 16, 16, 256, A * 3 + 64) == _lib.WUSH_EINVAL  # C overlaps b_codes
+    assert g(*args, 16, 16, 384, B) == _lib.WUSH_EINVAL
+    assert b"multiple of 256" in lib.wush_last_error()

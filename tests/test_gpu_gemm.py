@@ -1,0 +1,170 @@
+"""GPU parity of the MXFP4 GEMM (deep dive, section 3.4.6, Eq. 10).
+
+The HIP kernel is called through the C ABI and compared with ``oracle.gemm``
+on the same seeded operands.
+
+Bar:
+  * Exact cases.  Operands whose every partial sum is an fp32 number (small
+    scale spread, bounded K) must match bit for bit, in fp32 and, after
+    round-to-nearest-even, in bf16.  This pins nibble order, operand
+    orientation, scale placement and the ragged edges.
+  * General cases.  Each product of two E2M1 values and two E8M0 scales is
+    exact in fp32, so any fp32 summation order of the K products errs by at
+    most (K - 1) * 2^-24 * sum_k |a_k b_k|.  That is the tolerance, with
+    2^-8 * |C| added for a bf16 output (half an ulp, doubled for the input's
+    own fp32 error).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import codecs, gemm, quant
+from oracle import transform as tr
+from synthetic import CONFIGS, f64_to_bf16_bits, gen_calibration, gen_weight, gen_x_rows
+from synthetic.gemm_operands import GEMM_TOKENS, QWEN3_8B_LAYERS, gen_mx_operand
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import mxfp4_activation_amd as wush
+
+    wush.load()
+    yield
+
+
+def _dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _gemm(ac, asc, bc, bsc, out_dtype):
+    from mxfp4_activation_amd import ops
+
+    C = ops.gemm_mxfp4(_dev(ac), _dev(asc), _dev(bc), _dev(bsc), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    if out_dtype == torch.bfloat16:
+        return C.view(torch.int16).cpu().numpy().view(np.uint16)
+    return C.cpu().numpy()
+
+
+def _bf16_value(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _check_tol(got, ref, absref, K, bf16):
+    tol = (K - 1) * 2.0**-24 * absref
+    if bf16:
+        got = _bf16_value(got)
+        tol = tol + 2.0**-8 * np.abs(ref)
+    err = np.abs(got.astype(np.float64) - ref)
+    ratio = np.max(err / np.maximum(tol, 1e-300)) if err.size else 0.0
+    assert np.all(err <= tol), f"max err/tol {ratio:.3g}"
+    return ratio
+
+
+_EXACT = [
+    (1, 1, 256, 126, 128),
+    (7, 33, 256, 126, 128),
+    (128, 128, 512, 126, 128),
+    (129, 257, 1024, 126, 128),
+    (200, 130, 768, 126, 128),
+    (300, 64, 2048, 127, 127),
+    (5, 300, 256, 127, 127),
+]
+
+
+@pytest.mark.parametrize("M,N,K,slo,shi", _EXACT)
+def test_exact_small_integer_products(M, N, K, slo, shi):
+    ac, asc = gen_mx_operand(M, K, seed=100 + M, scale_lo=slo, scale_hi=shi)
+    bc, bsc = gen_mx_operand(N, K, seed=200 + N, scale_lo=slo, scale_hi=shi)
+    ref = gemm.gemm_mxfp4_ref(ac, asc, bc, bsc)
+    assert np.all(ref.astype(np.float32).astype(np.float64) == ref)  # the case is exact in fp32
+    got = _gemm(ac, asc, bc, bsc, torch.float32)
+    np.testing.assert_array_equal(got.astype(np.float64), ref)
+    got16 = _gemm(ac, asc, bc, bsc, torch.bfloat16)
+    np.testing.assert_array_equal(got16, codecs.f32_to_bf16_bits(ref.astype(np.float32)))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 4096), (77, 390, 1280), (513, 129, 256)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_wide_scale_range_within_fp32_bound(M, N, K, out):
+    ac, asc = gen_mx_operand(M, K, seed=7 + K, scale_lo=105, scale_hi=140)
+    bc, bsc = gen_mx_operand(N, K, seed=8 + K, scale_lo=110, scale_hi=135)
+    ref = gemm.gemm_mxfp4_ref(ac, asc, bc, bsc)
+    absref = gemm.gemm_mxfp4_abs_ref(ac, asc, bc, bsc)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    ratio = _check_tol(_gemm(ac, asc, bc, bsc, dt), ref, absref, K, out == "bf16")
+    print(f"max err / bound = {ratio:.3g}")
+
+
+@pytest.mark.parametrize("layer", ["q_proj", "k_proj", "gate_proj", "down_proj"])
+def test_qwen3_8b_layer_shapes_sampled(layer):
+    """Full-size operands (1024 tokens); a grid of sampled rows and columns,
+    including the first and last ones of every edge tile, is checked."""
+    N, K = QWEN3_8B_LAYERS[layer]
+    M = GEMM_TOKENS
+    ac, asc = gen_mx_operand(M, K, seed=31, scale_lo=112, scale_hi=124)
+    bc, bsc = gen_mx_operand(N, K, seed=32, scale_lo=116, scale_hi=122)
+    got = _gemm(ac, asc, bc, bsc, torch.float32)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.r_[0, 127, 128, M - 1, rng.choice(M, 20, replace=False)])
+    cols = np.unique(np.r_[0, 127, 128, N - 1, rng.choice(N, 20, replace=False)])
+    ref = gemm.gemm_mxfp4_ref(ac[rows], asc[rows], bc[cols], bsc[cols])
+    absref = gemm.gemm_mxfp4_abs_ref(ac[rows], asc[rows], bc[cols], bsc[cols])
+    _check_tol(got[np.ix_(rows, cols)], ref, absref, K, False)
+
+
+def test_zero_rows_is_a_no_op():
+    from mxfp4_activation_amd import ops
+
+    ac, asc = gen_mx_operand(0, 256, seed=1)
+    bc, bsc = gen_mx_operand(8, 256, seed=2)
+    C = ops.gemm_mxfp4(_dev(ac), _dev(asc), _dev(bc), _dev(bsc), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert C.shape == (0, 8)
+
+
+def test_quantized_layer_forward():
+    """Quantize activations with T_wush and weights with T_xvsh on the GPU,
+    multiply on the GPU, and compare with the oracle's quantize + multiply.
+
+    Where the GPU codes equal the oracle's (all but tie cases), the GEMM
+    output is held to the fp32 bound; the forward itself must recover
+    x^T w as closely as the oracle's does."""
+    from mxfp4_activation_amd import ops
+
+    wl = CONFIGS["tiny_mxfp4"]
+    x_bits = gen_x_rows(wl, 0, wl.M)
+    W = gen_weight(wl)
+    w_bits = f64_to_bf16_bits(W)
+    Tw, Tx = tr.build_transforms(W, gen_calibration(wl), wl.G)
+    tw_bits, tx_bits = tr.transforms_to_bf16_bits(Tw), tr.transforms_to_bf16_bits(Tx)
+
+    def dev_bf16(b):
+        return _dev(b.view(np.int16)).view(torch.bfloat16)
+
+    xc_g, xs_g = ops.quant("mxfp4", dev_bf16(x_bits), dev_bf16(tw_bits))
+    wc_g, ws_g = ops.quant("mxfp4", dev_bf16(w_bits), dev_bf16(tx_bits))
+    C_g = ops.gemm_mxfp4(xc_g, xs_g, wc_g, ws_g, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    C_g = C_g.cpu().numpy().astype(np.float64)
+
+    xc, xs = quant.run_path("mxfp4", x_bits, tw_bits)
+    wc, ws = quant.run_path("mxfp4", w_bits, tx_bits)
+    same_rows = np.all(xc_g.cpu().numpy() == xc, axis=1) & np.all(xs_g.cpu().numpy() == xs, axis=1)
+    same_cols = np.all(wc_g.cpu().numpy() == wc, axis=1) & np.all(ws_g.cpu().numpy() == ws, axis=1)
+    assert same_rows.mean() > 0.9 and same_cols.mean() > 0.9
+    ref = gemm.gemm_mxfp4_ref(xc, xs, wc, ws)
+    absref = gemm.gemm_mxfp4_abs_ref(xc, xs, wc, ws)
+    sel = np.ix_(same_rows, same_cols)
+    _check_tol(C_g[sel], ref[sel], absref[sel], wl.K, False)
+
+    x = _bf16_value(x_bits)
+    exact = x @ _bf16_value(w_bits).T
+    rel_gpu = np.linalg.norm(C_g - exact) / np.linalg.norm(exact)
+    rel_ref = np.linalg.norm(ref - exact) / np.linalg.norm(exact)
+    assert rel_gpu <= rel_ref * 1.01 + 1e-6, (rel_gpu, rel_ref)
