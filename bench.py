@@ -88,6 +88,9 @@ def parse():
     ap.add_argument("--compare-transforms", action="store_true",
                     help="instead of the step benchmark, time all transform banks through the same kernel, "
                          "interleaved in one process, and print one JSON line")
+    ap.add_argument("--gemm-layers", action="store_true",
+                    help="per-layer Eq. 10 forward (transform + quantize + MXFP4 GEMM) against the bf16 GEMM "
+                         "on Qwen3-8B layer shapes at 1024 tokens, instead of the headline measurement")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="instead of running, read four rocprofv3 --pmc output folders (FETCH_SIZE and "
                          "WRITE_SIZE of the path, then of --copy-probe-mib) and write "
@@ -342,6 +345,108 @@ def compare_transforms(args) -> None:
     }), flush=True)
 
 
+def gemm_layers(args) -> None:
+    """Per-layer forward of Eq. 10 on Qwen3-8B linear-layer shapes at 1024
+    tokens, against the bf16 GEMM (deep dive, section 3.4.7 and the
+    results: speedup of transform + quantization + FP4 MatMul over BF16,
+    with "None" = the FP4 MatMul alone).  Weights are random N(0, 0.02) in
+    nn.Linear order, pre-quantized offline with the weight-side transform
+    (T_xvsh for WUSH, H for H+Quant); activations are Student-t(3)-like
+    with 1% outlier channels.  Hot caches (the same buffers every step),
+    one HIP graph per variant, replays interleaved, median."""
+    import statistics
+
+    import torch
+
+    from mxfp4_activation_amd import ops, transforms
+    from synthetic.gemm_operands import GEMM_TOKENS, QWEN3_8B_LAYERS
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M, G = GEMM_TOKENS, 32
+    gen = torch.Generator(device="cpu").manual_seed(2024)
+    shapes = {}
+    for name, nk in QWEN3_8B_LAYERS.items():
+        shapes.setdefault(nk, []).append(name)
+    rows = []
+    for (N, K), names in shapes.items():
+        C = K // G
+        out_ch = torch.randperm(K, generator=gen)[: max(1, K // 100)]
+        def acts(n):
+            x = torch.distributions.StudentT(3.0).sample((n, K)) * 0.5
+            x[:, out_ch] *= 30.0
+            return x
+        torch.manual_seed(K * 7 + N)
+        Xcal = acts(2048).double()
+        W = (torch.randn(N, K, generator=gen, dtype=torch.float64) * 0.02)
+        Tw, Tx = transforms.wush_transforms(W, Xcal, G)
+        Hb = transforms.hadamard_transforms(C, G)
+        X = acts(M).to(torch.bfloat16).to(dev)
+        Wb = W.to(torch.bfloat16).to(dev)
+        banks = {"wush": (transforms.to_kernel_layout(Tw).to(dev), transforms.to_kernel_layout(Tx).to(dev)),
+                 "hadamard": (transforms.to_kernel_layout(Hb).to(dev),) * 2}
+        wq = {k: ops.quant("mxfp4", Wb, tb[1]) for k, tb in banks.items()}
+        xc = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        xs = torch.empty((M, K // G), dtype=torch.uint8, device=dev)
+        Cout = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        Wt = Wb.t()
+
+        def v_bf16():
+            torch.matmul(X, Wt, out=Cout)
+
+        def v_q(k):
+            def f():
+                ops.quant("mxfp4", X, banks[k][0], codes=xc, scales=xs)
+                ops.gemm_mxfp4(xc, xs, wq[k][0], wq[k][1], out_dtype=torch.bfloat16, out=Cout)
+            return f
+
+        def v_none():
+            ops.gemm_mxfp4(xc, xs, wq["wush"][0], wq["wush"][1], out_dtype=torch.bfloat16, out=Cout)
+
+        variants = {"bf16": v_bf16, "wush_quant_fp4": v_q("wush"), "h_quant_fp4": v_q("hadamard"),
+                    "none_fp4": v_none}
+        reps = 40
+        cap = torch.cuda.Stream()
+        graphs = {}
+        for vn, fn in variants.items():
+            with torch.cuda.stream(cap):
+                for _ in range(3):
+                    fn()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=cap):
+                for _ in range(reps):
+                    fn()
+            gr.replay()
+            graphs[vn] = gr
+        torch.cuda.synchronize()
+        times = {vn: [] for vn in variants}
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(7):
+            for vn in variants:
+                torch.cuda.synchronize()
+                e0.record()
+                graphs[vn].replay()
+                e1.record()
+                torch.cuda.synchronize()
+                times[vn].append(e0.elapsed_time(e1) * 1e3 / reps)
+        us = {vn: statistics.median(t) for vn, t in times.items()}
+        flop = 2.0 * M * N * K
+        row = {"layers": names, "N": N, "K": K, "M": M,
+               "us": {vn: round(t, 2) for vn, t in us.items()},
+               "speedup_vs_bf16": {vn: round(us["bf16"] / t, 2) for vn, t in us.items() if vn != "bf16"},
+               "fp4_gemm_tflops": round(flop / us["none_fp4"] / 1e6, 1),
+               "bf16_gemm_tflops": round(flop / us["bf16"] / 1e6, 1)}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    print(json.dumps({"comparison": "Eq. 10 forward per Qwen3-8B layer shape, 1024 tokens, bf16 output, hot caches",
+                      "variants": {"bf16": "torch.matmul (hipBLASLt)",
+                                   "wush_quant_fp4": "wush_quant_mxfp4 (T_wush) + wush_gemm_mxfp4",
+                                   "h_quant_fp4": "same kernels with the blockwise Hadamard bank",
+                                   "none_fp4": "wush_gemm_mxfp4 alone"},
+                      "layers": rows}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -359,6 +464,9 @@ def main():
         return
     if args.compare_transforms:
         compare_transforms(args)
+        return
+    if args.gemm_layers:
+        gemm_layers(args)
         return
 
     import numpy as np

@@ -14,22 +14,38 @@
 // the low nibble of byte t) and that block's E8M0 scale byte, which is
 // exactly the row-major layout the quantization kernel writes.
 //
-// Workgroup: a 128 x 128 tile of C, K in steps of 256 (128 code bytes per
-// row), 8 waves in two groups of 4.  Group g takes the steps ks = g, g + 2,
-// g + 4, ... (the K sum is split inside the workgroup), and the two partial
-// tiles are added through LDS at the end.  The split puts two waves on
-// every SIMD, so one wave's MFMAs cover the other's LDS latency, while the
-// output tile, and with it the global traffic per FLOP, stays 128 x 128.
-// Within a group, wave (wm, wn) owns a 64 x 64 quarter: 2 x 2 MFMA tiles of
-// 32 x 32.
+// Workgroup: a 128 x 128 tile of C and 8 waves in two groups of 4.  K runs
+// in steps of 256 elements (128 code bytes per row); group g takes the
+// second half-range [128 g, 128 g + 128) of every step (the K sum is split
+// inside the workgroup) and the two partial tiles are added through LDS at
+// the end.  Every SIMD holds one wave of each group.  Within a group, wave
+// (wm, wn) owns a 64 x 64 quarter: 2 x 2 MFMA tiles of 32 x 32.
 //
-// Codes are staged through LDS with row-contiguous 16-byte loads (rows
-// padded to 144 B, so the operand reads of 16 rows hit 16 distinct bank
-// groups); each row's 8 scale bytes of a step are regrouped so that lane
-// half h finds blocks h, h+2, h+4, h+6 in one word, and sub-step s selects
-// byte s with the instruction's op_sel.  Each group double-buffers its LDS
-// stage and keeps its global loads three of its steps ahead through two
-// register sets.
+// Operands go from global memory straight into LDS (global_load_lds, 16 B
+// per lane, whole 128-byte rows), through a ring of 4 step stages, two
+// steps ahead of the MFMAs.  No staging registers and no LDS write
+// instructions are involved; each wave waits for its own loads with vmcnt
+// and one barrier per step publishes them.
+//
+// LDS layout of a stage: A codes [128 rows][128 B], B codes [128][128 B], A
+// scales [128][8 B], B scales [128][8 B].  A load instruction writes 1 KB
+// contiguously (8 rows), so rows are not padded: the 16-byte chunk c of
+// row r sits in slot c ^ ((r >> 1) & 7) instead, which gives the operand
+// reads of 16 consecutive rows 16 distinct bank groups.  Sub-step s of a
+// step gives lane (i + 32h) chunk 2 s + h of row i, i.e. K block 2 s + h,
+// whose E8M0 scale is byte 2 s + h of the row's 8 scale bytes; the scale
+// word is shifted right by 8 h so that op_sel 2 (s % 2) picks it for both
+// lane halves.
+//
+// Fragment reads are inline-asm ds_read blocks that wait for their own
+// results: plain LDS loads after a global_load_lds make the compiler wait
+// for every outstanding global load, which would drain the ring.  Group 1
+// runs its MFMAs before its reads in every step (on registers read in the
+// step before), so that on each SIMD one wave reads LDS while the other
+// keeps the matrix unit busy.
+//
+// The result goes through LDS once more, so that C is written with 16-byte
+// row-contiguous stores.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,115 +59,93 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128, BN = 128;
-constexpr int BK_BYTES = 128;            // code bytes per row per K step (256 elements)
-constexpr int kRowB = BK_BYTES + 16;     // padded LDS row
+constexpr int kRowB = 128;                // code bytes per row per step (256 elements)
+constexpr int kStages = 4;
+constexpr int kAhead = 2;                 // steps of loads in flight (a third measured no faster)
 constexpr int kGroups = 2;
 constexpr int kThreads = 256 * kGroups;
-
-struct GemmLds {
-  uint8_t a[kGroups][2][BM * kRowB];
-  uint8_t b[kGroups][2][BN * kRowB];
-  uint32_t sa[kGroups][2][BM * 2];  // row r: word h = scale bytes of blocks h, h+2, h+4, h+6
-  uint32_t sb[kGroups][2][BN * 2];
-};
-// The final exchange of partial tiles reuses the stage buffers: 8 waves x
-// 2 tiles x 16 floats x 64 lanes.
-static_assert(sizeof(((GemmLds*)0)->a) >= 8 * 2 * 16 * 64 * 4, "exchange does not fit");
+constexpr int kOffB = BM * kRowB;                      // 16384
+constexpr int kOffSA = kOffB + BN * kRowB;             // 32768
+constexpr int kOffSB = kOffSA + BM * 8;                // 33792
+constexpr int kStageB = kOffSB + BN * 8;               // 34816
+constexpr int kLdsB = kStages * kStageB;               // 139264
+constexpr int kLoadsPerStep = 5;                       // load instructions per wave per step
+constexpr int kCRow = BN + 4;                          // padded fp32 row of the output tile in LDS
+static_assert(kLdsB >= 8 * 2 * 16 * 64 * 4, "exchange does not fit");
+static_assert(kLdsB >= BM * kCRow * 4, "output tile does not fit");
+static_assert(kStages >= kAhead + 1, "ring too short for the load distance");
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
-// Eight scale bytes b0..b7 (blocks 0..7 of the step, b0 lowest) ->
-// {b0 b2 b4 b6}, {b1 b3 b5 b7}.
-__device__ __forceinline__ u32x2 regroup_scales(u32x2 v) {
-  // v_perm_b32(src0, src1, sel): byte selectors 0..3 pick src1, 4..7 src0.
-  const uint32_t even = __builtin_amdgcn_perm(v[1], v[0], 0x06040200u);
-  const uint32_t odd = __builtin_amdgcn_perm(v[1], v[0], 0x07050301u);
-  u32x2 r = {even, odd};
-  return r;
-}
-
-template <int SUB>
+template <int OPSEL>
 __device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, u32x4 b, f32x16 c, uint32_t sa, uint32_t sb) {
   const i32x8 a8 = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
   const i32x8 b8 = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
-  // format 4 = E2M1 for both operands; op_sel SUB picks scale byte SUB.
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, SUB, (int)sa, SUB, (int)sb);
+  // format 4 = E2M1 for both operands; op_sel picks the scale byte.
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, OPSEL, (int)sa, OPSEL, (int)sb);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   const uint32_t b = __float_as_uint(x);
-  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef const __attribute__((address_space(1))) uint8_t glb_u8;
 
 template <bool BF16_OUT>
 __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) GemmLds L;
+  __shared__ __attribute__((aligned(1024))) uint8_t L[kLdsB];
+  lds_u8* const Ls = (lds_u8*)L;
+  const uint32_t lbase = (uint32_t)(uintptr_t)Ls;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
   const int grp = wave >> 2;      // K-split group
   const int gw = wave & 3;        // wave within the group
-  const int gt = tid & 255;       // thread within the group
   const int wm = gw >> 1, wn = gw & 1;
   const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
   const int64_t K = g.K, M = g.M, N = g.N;
   const int64_t row_bytes = K / 2, row_scales = K / 32;
   const int nk = (int)(K / 256);
-  const int nj = (nk + 1) / 2;    // steps per group (group 1 idles on the last one when nk is odd)
 
-  // Staging map (per group): thread t moves 16-byte chunk t % 8 of rows
-  // t / 8 + 32 q (q = 0..3) of both tiles; threads 0..127 move A scale
-  // rows, 128..255 B.
-  const int c_chunk = gt & 7, c_row = gt >> 3;
-  const uint8_t* a_src[4];
-  const uint8_t* b_src[4];
+  // Load map.  Code loads: wave w moves rows 16 w + 8 q .. +7 (q = 0, 1) of
+  // both tiles; lane L takes row L / 8 of those 8 and stores LDS slot L % 8,
+  // which holds chunk (L % 8) ^ ((4 q + L / 16) % 8).
+  glb_u8* a_src[2];
+  glb_u8* b_src[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int64_t ra = m0 + c_row + 32 * q, rb = n0 + c_row + 32 * q;
+  for (int q = 0; q < 2; ++q) {
+    const int r = 16 * wave + 8 * q + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((4 * q + (lane >> 4)) & 7);
+    int64_t ra = m0 + r, rb = n0 + r;
     ra = ra < M ? ra : M - 1;  // rows past the edge reload the last row; never stored
     rb = rb < N ? rb : N - 1;
-    a_src[q] = g.a_codes + ra * row_bytes + 16 * c_chunk;
-    b_src[q] = g.b_codes + rb * row_bytes + 16 * c_chunk;
+    a_src[q] = (glb_u8*)g.a_codes + ra * row_bytes + 16 * chunk;
+    b_src[q] = (glb_u8*)g.b_codes + rb * row_bytes + 16 * chunk;
   }
-  const bool scale_a = gt < 128;
-  const int s_row = gt & 127;
-  int64_t s_r = (scale_a ? m0 : n0) + s_row;
-  const int64_t s_lim = scale_a ? M : N;
-  s_r = s_r < s_lim ? s_r : s_lim - 1;
-  const uint8_t* s_src = (scale_a ? g.a_scales : g.b_scales) + s_r * row_scales;
+  // Scale loads: waves 0..3 move A rows 32 w + L / 2, waves 4..7 B rows
+  // 32 (w - 4) + L / 2, 4 bytes (half a row's 8) per lane.
+  const bool s_is_a = wave < 4;
+  int64_t s_row = (s_is_a ? m0 : n0) + 32 * (wave & 3) + (lane >> 1);
+  const int64_t s_lim = s_is_a ? M : N;
+  s_row = s_row < s_lim ? s_row : s_lim - 1;
+  glb_u8* s_src = (glb_u8*)(s_is_a ? g.a_scales : g.b_scales) + s_row * row_scales + 4 * (lane & 1);
+  const int s_dst = (s_is_a ? kOffSA : kOffSB) + 256 * (wave & 3);
 
-  // Group step j covers K step 2 j + grp.  Past the end the index is
-  // clamped: the load repeats a valid step and nothing is computed from it.
-  auto kstep = [&](int j) { return min(2 * j + grp, nk - 1); };
-
-  // Two register sets carry global data two group steps ahead of its use:
-  // step j stages set (j + 1) & 1 (the operands of step j + 1) into LDS and
-  // then refills that set with step j + 3.
-  struct Regs {
-    u32x4 a[4], b[4];
-    u32x2 s;
-  };
-  Regs R0, R1;
-  auto load = [&](Regs& r, int j) {
-    const int64_t off = (int64_t)kstep(j) * BK_BYTES;
+  // Step ks lives in ring stage ks % 4.
+  auto issue = [&](int ks) {
+    const int64_t kc = ks;
+    lds_u8* st = Ls + (ks % kStages) * kStageB;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      r.a[q] = *reinterpret_cast<const u32x4*>(a_src[q] + off);
-      r.b[q] = *reinterpret_cast<const u32x4*>(b_src[q] + off);
+    for (int q = 0; q < 2; ++q) {
+      __builtin_amdgcn_global_load_lds(a_src[q] + kc * kRowB, st + 1024 * (2 * wave + q), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(b_src[q] + kc * kRowB, st + kOffB + 1024 * (2 * wave + q), 16, 0, 0);
     }
-    r.s = *reinterpret_cast<const u32x2*>(s_src + (int64_t)kstep(j) * 8);
-  };
-  auto stage = [&](const Regs& r, int buf) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      *reinterpret_cast<u32x4*>(L.a[grp][buf] + (c_row + 32 * q) * kRowB + 16 * c_chunk) = r.a[q];
-      *reinterpret_cast<u32x4*>(L.b[grp][buf] + (c_row + 32 * q) * kRowB + 16 * c_chunk) = r.b[q];
-    }
-    const u32x2 w = regroup_scales(r.s);
-    uint32_t* dst = scale_a ? L.sa[grp][buf] : L.sb[grp][buf];
-    *reinterpret_cast<u32x2*>(dst + 2 * s_row) = w;
+    __builtin_amdgcn_global_load_lds(s_src + kc * 8, st + s_dst, 4, 0, 0);
   };
 
   f32x16 acc[2][2];
@@ -160,63 +154,96 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
+  // Per-lane parts of the fragment addresses: group g runs sub-steps 2 g and
+  // 2 g + 1, i.e. chunks 4 g + h and 4 g + 2 + h, and scale word g.
   const int li = lane & 31, lh = lane >> 5;
-  auto compute = [&](int buf) {
-    const uint8_t* la = L.a[grp][buf];
-    const uint8_t* lb = L.b[grp][buf];
-    uint32_t sa[2], sb[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sa[t] = L.sa[grp][buf][2 * (64 * wm + 32 * t + li) + lh];
-      sb[t] = L.sb[grp][buf][2 * (64 * wn + 32 * t + li) + lh];
-    }
-#define WUSH_GEMM_SUB(S)                                                                                   \
-    {                                                                                                     \
-      u32x4 av[2], bv[2];                                                                                 \
-      _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                                     \
-        av[t] = *reinterpret_cast<const u32x4*>(la + (64 * wm + 32 * t + li) * kRowB + 32 * (S) + 16 * lh); \
-        bv[t] = *reinterpret_cast<const u32x4*>(lb + (64 * wn + 32 * t + li) * kRowB + 32 * (S) + 16 * lh); \
-      }                                                                                                   \
-      _Pragma("unroll") for (int i = 0; i < 2; ++i) _Pragma("unroll") for (int j = 0; j < 2; ++j)         \
-          acc[i][j] = mfma_fp4<S>(av[i], bv[j], acc[i][j], sa[i], sb[j]);                                \
-    }
-    WUSH_GEMM_SUB(0)
-    WUSH_GEMM_SUB(1)
-    WUSH_GEMM_SUB(2)
-    WUSH_GEMM_SUB(3)
-#undef WUSH_GEMM_SUB
+  const int sw = (li >> 1) & 7;
+  const uint32_t fa0 = (64 * wm + li) * kRowB + 16 * ((4 * grp + lh) ^ sw);
+  const uint32_t fa1 = (64 * wm + li) * kRowB + 16 * ((4 * grp + 2 + lh) ^ sw);
+  const uint32_t fb0 = kOffB + (64 * wn + li) * kRowB + 16 * ((4 * grp + lh) ^ sw);
+  const uint32_t fb1 = kOffB + (64 * wn + li) * kRowB + 16 * ((4 * grp + 2 + lh) ^ sw);
+  const uint32_t fsa = kOffSA + 8 * (64 * wm + li) + 4 * grp;
+  const uint32_t fsb = kOffSB + 8 * (64 * wn + li) + 4 * grp;
+  const uint32_t shift = 8 * lh;
+
+  struct Frag {
+    u32x4 a00, a01, a10, a11, b00, b01, b10, b11;  // [sub-step][tile]
+    uint32_t sa0, sa1, sb0, sb1;
+  };
+  auto read = [&](int ks, Frag& f) {
+    const uint32_t st = lbase + (ks % kStages) * kStageB;
+    // Tile row / column t = 1 is 32 rows further: 4096 B of codes, 256 B of scales.
+    asm volatile(
+        "ds_read_b128 %0, %12\n"
+        "ds_read_b128 %1, %12 offset:4096\n"
+        "ds_read_b128 %2, %13\n"
+        "ds_read_b128 %3, %13 offset:4096\n"
+        "ds_read_b128 %4, %14\n"
+        "ds_read_b128 %5, %14 offset:4096\n"
+        "ds_read_b128 %6, %15\n"
+        "ds_read_b128 %7, %15 offset:4096\n"
+        "ds_read_b32 %8, %16\n"
+        "ds_read_b32 %9, %16 offset:256\n"
+        "ds_read_b32 %10, %17\n"
+        "ds_read_b32 %11, %17 offset:256\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a00), "=&v"(f.a01), "=&v"(f.a10), "=&v"(f.a11), "=&v"(f.b00), "=&v"(f.b01), "=&v"(f.b10),
+          "=&v"(f.b11), "=&v"(f.sa0), "=&v"(f.sa1), "=&v"(f.sb0), "=&v"(f.sb1)
+        : "v"(st + fa0), "v"(st + fa1), "v"(st + fb0), "v"(st + fb1), "v"(st + fsa), "v"(st + fsb)
+        : "memory");
+    f.sa0 >>= shift;
+    f.sa1 >>= shift;
+    f.sb0 >>= shift;
+    f.sb1 >>= shift;
+  };
+  auto mfma = [&](const Frag& f) {
+    acc[0][0] = mfma_fp4<0>(f.a00, f.b00, acc[0][0], f.sa0, f.sb0);
+    acc[0][1] = mfma_fp4<0>(f.a00, f.b01, acc[0][1], f.sa0, f.sb1);
+    acc[1][0] = mfma_fp4<0>(f.a01, f.b00, acc[1][0], f.sa1, f.sb0);
+    acc[1][1] = mfma_fp4<0>(f.a01, f.b01, acc[1][1], f.sa1, f.sb1);
+    acc[0][0] = mfma_fp4<2>(f.a10, f.b10, acc[0][0], f.sa0, f.sb0);
+    acc[0][1] = mfma_fp4<2>(f.a10, f.b11, acc[0][1], f.sa0, f.sb1);
+    acc[1][0] = mfma_fp4<2>(f.a11, f.b10, acc[1][0], f.sa1, f.sb0);
+    acc[1][1] = mfma_fp4<2>(f.a11, f.b11, acc[1][1], f.sa1, f.sb1);
   };
 
-  // Group step j: barrier (this group's buffer j & 1 is complete and its
-  // waves are done with buffer (j + 1) & 1), stage step j + 1, refill,
-  // compute step j.  Loads and stages run unconditionally so the load
-  // counter at every stage is the same on all paths.
-  auto step = [&](int j, Regs& next) {
-    __syncthreads();
-    stage(next, (j + 1) & 1);
-    load(next, j + 3);
-    // Keep the refill ahead of this step's MFMAs; the scheduler would
-    // otherwise sink it below them and halve the latency it hides.
-    __builtin_amdgcn_sched_barrier(0);
-    if (2 * j + grp < nk) compute(j & 1);
+  // Step ks: wait for this wave's loads of step ks (those of the later
+  // steps already issued may stay in flight), barrier (every wave's loads
+  // of step ks have landed, and every wave is done with the stage step
+  // ks - 1 used), refill that stage with step ks + kAhead if there is one.
+  // Group 0 then reads step ks and runs its MFMAs; group 1 first runs the
+  // MFMAs of step ks - 1 from registers and reads step ks last, so that on
+  // each SIMD one wave reads LDS while the other keeps the matrix unit busy.
+  auto sync = [&](int ks) {
+    if (ks + 1 < nk)  // step ks + 1 was issued after ks and may stay in flight
+      asm volatile("s_waitcnt vmcnt(%0)\n s_barrier" ::"n"(kLoadsPerStep) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n s_barrier" ::: "memory");
+    if (ks + kAhead < nk) issue(ks + kAhead);
   };
-
-  load(R0, 0);
-  load(R1, 1);
-  stage(R0, 0);
-  load(R0, 2);
-  int j = 0;
-  for (; j + 1 < nj; j += 2) {
-    step(j, R1);
-    step(j + 1, R0);
+  static_assert(kAhead == 2, "sync() spells out the wait counts for two steps in flight");
+  for (int p = 0; p < kAhead; ++p)
+    if (p < nk) issue(p);
+  Frag f;
+  if (grp == 0) {
+    for (int ks = 0; ks < nk; ++ks) {
+      sync(ks);
+      read(ks, f);
+      mfma(f);
+    }
+  } else {
+    for (int ks = 0; ks < nk; ++ks) {
+      sync(ks);
+      if (ks > 0) mfma(f);
+      read(ks, f);
+    }
+    mfma(f);
   }
-  if (j < nj) step(j, R1);
+  asm volatile("s_waitcnt vmcnt(0)\n s_barrier" ::: "memory");
 
   // Add the two groups' partial tiles: group g finishes MFMA tile row
   // i == g of its quarter and hands tile row 1 - g to its partner wave.
-  __syncthreads();
-  float* xch = reinterpret_cast<float*>(&L.a[0][0][0]);
-  const int partner = wave ^ 4;
+  f32x4* xch = reinterpret_cast<f32x4*>(L);
   f32x16 give[2], fin[2];
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt) {  // constant indices keep acc in registers
@@ -226,28 +253,60 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xch[((wave * 2 + jt) * 16 + r) * 64 + lane] = give[jt][r];
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = {give[jt][4 * q], give[jt][4 * q + 1], give[jt][4 * q + 2], give[jt][4 * q + 3]};
+      xch[((wave * 2 + jt) * 4 + q) * 64 + lane] = v;
+    }
   __syncthreads();
+  const int partner = wave ^ 4;
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) fin[jt][r] += xch[((partner * 2 + jt) * 16 + r) * 64 + lane];
-
-  // Epilogue: lane (j + 32h) of MFMA tile (i, jt) holds C rows
-  // 8 (r / 4) + 4 h + r % 4 of column j; a half-wave writes 32 consecutive
-  // columns of one row.
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = xch[((partner * 2 + jt) * 4 + q) * 64 + lane];
 #pragma unroll
-  for (int jt = 0; jt < 2; ++jt) {
-    const int64_t col = n0 + 64 * wn + 32 * jt + li;
-    if (col >= N) continue;
+      for (int e = 0; e < 4; ++e) fin[jt][4 * q + e] += v[e];
+    }
+  __syncthreads();
+
+  // Output tile to LDS (fp32, rows padded): lane (j + 32h) of MFMA tile
+  // (grp, jt) holds rows 8 (r / 4) + 4 h + r % 4 of column j.
+  float* ct = reinterpret_cast<float*>(L);
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t row = m0 + 64 * wm + 32 * grp + 8 * (r / 4) + 4 * lh + (r % 4);
-      if (row < M) {
+      const int row = 64 * wm + 32 * grp + 8 * (r / 4) + 4 * lh + (r % 4);
+      ct[row * kCRow + 64 * wn + 32 * jt + li] = fin[jt][r];
+    }
+  __syncthreads();
+
+  // Row-contiguous stores: each thread writes 4 (fp32) or 8 (bf16) columns
+  // at a time.  Tiles cut by the matrix edge, or rows that are not 16-byte
+  // aligned, store element by element.
+  constexpr int kVec = BF16_OUT ? 8 : 4;
+  constexpr int kVecPerRow = BN / kVec;
+  const bool full = m0 + BM <= M && n0 + BN <= N && (N % kVec) == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15) == 0;
+  for (int v = tid; v < BM * kVecPerRow; v += kThreads) {
+    const int row = v / kVecPerRow, c0 = (v % kVecPerRow) * kVec;
+    const float* src = ct + row * kCRow + c0;
+    const int64_t grow = m0 + row, gcol = n0 + c0;
+    if (full) {
+      if (BF16_OUT) {
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16_rne(src[2 * e]) | (f32_to_bf16_rne(src[2 * e + 1]) << 16);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + grow * N + gcol) = o;
+      } else {
+        const f32x4 o = {src[0], src[1], src[2], src[3]};
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.C) + grow * N + gcol) = o;
+      }
+    } else if (grow < M) {
+      for (int e = 0; e < kVec && gcol + e < N; ++e) {
         if (BF16_OUT)
-          reinterpret_cast<uint16_t*>(g.C)[row * N + col] = f32_to_bf16_rne(fin[jt][r]);
+          reinterpret_cast<uint16_t*>(g.C)[grow * N + gcol + e] = (uint16_t)f32_to_bf16_rne(src[e]);
         else
-          reinterpret_cast<float*>(g.C)[row * N + col] = fin[jt][r];
+          reinterpret_cast<float*>(g.C)[grow * N + gcol + e] = src[e];
       }
     }
   }

@@ -99,7 +99,7 @@ def test_eq10_forward_recovers_product(transform):
     C = gemm.gemm_mxfp4_ref(xc, xs, wc, ws)
     ref = x @ W.T
     rel = np.linalg.norm(C - ref) / np.linalg.norm(ref)
-    assert rel < 0.2, rel
+    assert rel < (0.1 if transform == "wush" else 0.25), rel
     if transform == "wush":
         # The weight side must take T_xvsh: T_xvsh^T T_wush = I, while
         # T_wush^T T_wush is not the identity.
