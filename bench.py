@@ -91,6 +91,9 @@ def parse():
     ap.add_argument("--gemm-layers", action="store_true",
                     help="per-layer Eq. 10 forward (transform + quantize + MXFP4 GEMM) against the bf16 GEMM "
                          "on Qwen3-8B layer shapes at 1024 tokens, instead of the headline measurement")
+    ap.add_argument("--layer-loss", action="store_true",
+                    help="layerwise loss (Eq. 5) of I / H / WUS / WUSH in MXFP4, NVFP4 and INT4 on synthetic "
+                         "Qwen3-8B-shaped layers, computed by the kernels, instead of the headline measurement")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="instead of running, read four rocprofv3 --pmc output folders (FETCH_SIZE and "
                          "WRITE_SIZE of the path, then of --copy-probe-mib) and write "
@@ -447,6 +450,47 @@ def gemm_layers(args) -> None:
                       "layers": rows}), flush=True)
 
 
+def layer_loss(args) -> None:
+    """Table 1 analogue (deep dive, section 5, "Per-Layer Quantization
+    Loss"): Eq. 5 for the transform pairs I, H, WUS and WUSH in the three
+    formats, on one synthetic linear layer per Qwen3-8B block shape (random
+    N(0, 0.02) weights, Student-t(3) activations with 1% outlier channels,
+    2048 calibration and 2048 evaluation tokens).  Transform, quantization
+    and dequantization run in the kernels; the products are fp32 GEMMs.
+    Printed per layer and format: the loss and the loss relative to the
+    mean squared unquantized output."""
+    import numpy as np
+    import torch
+
+    from mxfp4_activation_amd import layerwise
+    from synthetic import f64_to_bf16_bits
+    from synthetic.gemm_operands import QWEN3_8B_LAYERS
+    from synthetic.layers import gen_linear_layer
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16(a):
+        return torch.from_numpy(f64_to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    table = {}
+    for li, (name, (N, K)) in enumerate(QWEN3_8B_LAYERS.items()):
+        W, Xc, Xe = gen_linear_layer(K, N, 2048, 2048, seed=7000 + li, n_outlier=max(1, K // 100))
+        X, Wd = bf16(Xe), bf16(W)
+        ref_ms = float((X.float() @ Wd.float().t()).double().pow(2).mean().item())
+        for fmt in ("mxfp4", "nvfp4", "int4"):
+            G = 16 if fmt == "nvfp4" else 32
+            banks = layerwise.transform_pairs(torch.from_numpy(W), torch.from_numpy(Xc), G, dev)
+            losses = {k: layerwise.layerwise_loss(fmt, X, Wd, a, b) for k, (a, b) in banks.items()}
+            row = {"layer": name, "d_in": K, "d_out": N, "format": fmt,
+                   "loss": {k: float("%.6g" % v) for k, v in losses.items()},
+                   "relative": {k: float("%.4g" % (v / ref_ms)) for k, v in losses.items()}}
+            table.setdefault(fmt, {})[name] = row["relative"]
+            print(json.dumps(row), flush=True)
+    print(json.dumps({"comparison": "layerwise loss (Eq. 5) relative to the mean squared output, synthetic "
+                                    "Qwen3-8B-shaped layers", "relative": table}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -467,6 +511,9 @@ def main():
         return
     if args.gemm_layers:
         gemm_layers(args)
+        return
+    if args.layer_loss:
+        layer_loss(args)
         return
 
     import numpy as np

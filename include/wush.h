@@ -126,6 +126,20 @@ wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const voi
                             const void* b_scales, int64_t M, int64_t N, int64_t K, void* C,
                             int out_type, hipStream_t stream);
 
+/* Dequantization: out[m][k] = the value code k of row m stands for,
+ *   MXFP4  e2m1(code) * 2^(scale - 127)                  (G = 32)
+ *   NVFP4  e2m1(code) * fp32(E4M3(scale) * g)            (G = 16)
+ *   INT4   code * fp16(scale)                            (G = 32)
+ * with codes and scales in the layouts the quantizers write.  This gives
+ * the quantized operands of the layerwise loss of Eq. 5 ("WUSH", deep dive,
+ * section 3.4.1): (d_out d_batch)^-1 ||q(T_W W)^T q(T_X X) - W^T X||_F^2.
+ *   fmt: 0 = MXFP4, 1 = NVFP4, 2 = INT4.  global_scale: device fp32, NVFP4 only.
+ *   out: fp32 [M][K], 16-byte aligned, must not overlap the inputs.
+ * K must be a positive multiple of 32 (MXFP4, INT4) or 16 (NVFP4); codes
+ * 8-byte aligned.  Errors as for wush_quant. */
+wush_status wush_dequant(int fmt, const void* codes, const void* scales, const float* global_scale, int64_t M,
+                         int64_t K, float* out, hipStream_t stream);
+
 /* Transform only: Y[m][cG+i] = sum_j T[c][i][j] x_(cG+j), in fp32 from the
  * matrix cores, without rounding fix-up.  G is 16 or 32.  Use it to check
  * values before quantization, or when the transformed activations are wanted

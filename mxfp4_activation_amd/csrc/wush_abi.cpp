@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/wush.h"
+#include "wush_dequant.h"
 #include "wush_gemm.h"
 #include "wush_kernels.h"
 
@@ -297,6 +298,31 @@ wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const voi
   g.N = N;
   g.K = K;
   hipError_t e = wush::launch_gemm_mxfp4(g, out_type == WUSH_OUT_BF16, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+wush_status wush_dequant(int fmt, const void* codes, const void* scales, const float* global_scale, int64_t M,
+                         int64_t K, float* out, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (fmt < 0 || fmt > 2) return fail(WUSH_EUNSUPPORTED, "unknown format %d", fmt);
+  const int G = fmt == 1 ? 16 : 32;
+  if (M < 0) return fail(WUSH_EINVAL, "M must be >= 0");
+  if (K <= 0 || K % G != 0) return fail(WUSH_EINVAL, "K must be a positive multiple of %d (got %lld)", G, (long long)K);
+  if (K > ((int64_t)1 << 30) || M > (INT64_MAX / 8) / K) return fail(WUSH_EINVAL, "sizes overflow");
+  if (M == 0) return WUSH_OK;
+  if ((M * (K / 16) + 255) / 256 > 0x7FFFFFFF) return fail(WUSH_EINVAL, "too large for one launch");
+  if (!codes || !scales || !out || (fmt == 1 && !global_scale)) return fail(WUSH_EINVAL, "null pointer");
+  if (!aligned(codes, 8)) return fail(WUSH_EALIGN, "codes must be 8-byte aligned");
+  if (fmt == 2 && !aligned(scales, 2)) return fail(WUSH_EALIGN, "INT4 scales must be 2-byte aligned");
+  if (fmt == 1 && !aligned(global_scale, 4)) return fail(WUSH_EALIGN, "global_scale must be 4-byte aligned");
+  if (!aligned(out, 16)) return fail(WUSH_EALIGN, "out must be 16-byte aligned");
+  const uint64_t no = (uint64_t)M * K * 4, nc = (uint64_t)M * K / 2, ns = (uint64_t)M * (K / G) * (fmt == 2 ? 2 : 1);
+  if (overlap(out, no, codes, nc) || overlap(out, no, scales, ns) || (fmt == 1 && overlap(out, no, global_scale, 4)))
+    return fail(WUSH_EINVAL, "out overlaps an input");
+  wush_status st = check_device();
+  if (st != WUSH_OK) return st;
+  hipError_t e = wush::launch_dequant(fmt, static_cast<const uint8_t*>(codes), scales, global_scale, M, K, out, stream);
   if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
   return WUSH_OK;
 }

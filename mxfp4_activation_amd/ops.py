@@ -79,6 +79,29 @@ def quant_int4(X, T, codes=None, scales=None):
     return quant("int4", X, T, codes=codes, scales=scales)
 
 
+def dequant(fmt: str, codes: torch.Tensor, scales: torch.Tensor, global_scale: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 values of quantized rows (codes [M][K/2], scales [M][K/G])."""
+    G = _G[fmt]
+    if codes.dtype != torch.uint8 or not codes.is_cuda or not codes.is_contiguous() or codes.dim() != 2:
+        raise ValueError("codes must be a contiguous 2-D uint8 device tensor")
+    M, K = codes.shape[0], codes.shape[1] * 2
+    sdt = torch.float16 if fmt == "int4" else torch.uint8
+    if scales.dtype != sdt or tuple(scales.shape) != (M, K // G) or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous %s tensor of shape (M, K/%d)" % (sdt, G))
+    if fmt == "nvfp4" and (global_scale is None or global_scale.dtype != torch.float32 or global_scale.numel() != 1):
+        raise ValueError("NVFP4 needs a one-element fp32 device global_scale")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=codes.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, K) or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    lib = _lib.load()
+    gs = global_scale.data_ptr() if fmt == "nvfp4" else None
+    _lib.check(lib.wush_dequant(_lib.FMT[fmt], codes.data_ptr(), scales.data_ptr(), gs, M, K, out.data_ptr(), _stream()),
+               "wush_dequant")
+    return out
+
+
 def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
                out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C[m][n] = sum_k a[m][k] b[n][k] for MXFP4 operands (codes [rows][K/2],

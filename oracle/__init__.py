@@ -21,6 +21,9 @@ Quantization", arXiv 2512.00956):
 * ``gemm``       is the FP4 matrix product that consumes the quantized
   activations and the pre-quantized weights (deep dive, section 3.4.6,
   Eq. 10): decode both MXFP4 operands, multiply in float64.
+* ``loss``       is the layerwise loss of Eq. 5 (deep dive, section 3.4.1):
+  quantize both operands through their block transforms, multiply, and
+  take the mean squared error against the unquantized product.
 * ``quant``      is the online path.  For every token and block it computes
   y = T_wush(c) x.  Then it applies RTN AbsMax quantization of y in groups
   of G, the transform block (deep dive, sections 3.4.1 and 3.4.7; Eq. 10).

@@ -98,3 +98,20 @@ def test_gemm_validation_rejects_bad_arguments():
     assert g(*args, 16, 16, 256, A * 3 + 64) == _lib.WUSH_EINVAL  # C overlaps b_codes
     assert g(*args, 16, 16, 384, B) == _lib.WUSH_EINVAL
     assert b"multiple of 256" in lib.wush_last_error()
+
+
+def test_dequant_validation_rejects_bad_arguments():
+    lib = wush.load()
+    B = A * 64
+    d = lambda fmt, c, s, g, M, K, o: lib.wush_dequant(fmt, c, s, g, M, K, o, None)
+    assert d(0, A, A * 2, None, 0, 64, B) == _lib.WUSH_OK  # M = 0: no-op
+    assert d(3, A, A * 2, None, 4, 64, B) == _lib.WUSH_EUNSUPPORTED
+    assert d(0, A, A * 2, None, -1, 64, B) == _lib.WUSH_EINVAL
+    assert d(0, A, A * 2, None, 4, 48, B) == _lib.WUSH_EINVAL  # MXFP4 needs K % 32
+    assert d(1, A, A * 2, None, 4, 48, B) == _lib.WUSH_EINVAL  # NVFP4 needs its global scale
+    assert d(1, A, A * 2, A * 3, 4, 40, B) == _lib.WUSH_EINVAL  # K % 16
+    assert d(0, A + 4, A * 2, None, 4, 64, B) == _lib.WUSH_EALIGN
+    assert d(2, A, A * 2 + 1, None, 4, 64, B) == _lib.WUSH_EALIGN
+    assert d(0, A, A * 2, None, 4, 64, B + 4) == _lib.WUSH_EALIGN
+    assert d(0, A, A * 2, None, 4, 64, A) == _lib.WUSH_EINVAL  # out overlaps codes
+    assert d(0, None, A * 2, None, 4, 64, B) == _lib.WUSH_EINVAL
