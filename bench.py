@@ -94,6 +94,9 @@ def parse():
     ap.add_argument("--layer-loss", action="store_true",
                     help="layerwise loss (Eq. 5) of I / H / WUS / WUSH in MXFP4, NVFP4 and INT4 on synthetic "
                          "Qwen3-8B-shaped layers, computed by the kernels, instead of the headline measurement")
+    ap.add_argument("--build-transforms", action="store_true",
+                    help="time the GPU transform construction (wush_build_transforms) against the torch float64 "
+                         "builder on each workload's layer, instead of the headline measurement")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="instead of running, read four rocprofv3 --pmc output folders (FETCH_SIZE and "
                          "WRITE_SIZE of the path, then of --copy-probe-mib) and write "
@@ -491,6 +494,49 @@ def layer_loss(args) -> None:
                                     "Qwen3-8B-shaped layers", "relative": table}), flush=True)
 
 
+def build_transforms_timing(args) -> None:
+    """Offline construction of T_wush and T_xvsh for each workload's layer
+    (Eq. 7, Eq. 8): the GPU kernel (moments, damping, Cholesky, Jacobi SVD,
+    products, one workgroup per block, float64) against the torch float64
+    builder on the host (batched LAPACK), with the largest difference
+    between the two relative to each block's largest entry."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    from mxfp4_activation_amd import ops, transforms
+    from synthetic import CONFIGS, f64_to_bf16_bits, gen_calibration, gen_weight
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    for name in ("llama8b_mxfp4", "downproj_mxfp4", "nvfp4", "int4"):
+        wl = CONFIGS[name]
+        W, Xc = gen_weight(wl), gen_calibration(wl)
+        Wd = torch.from_numpy(f64_to_bf16_bits(W).view(np.int16)).to(dev).view(torch.bfloat16)
+        Xd = torch.from_numpy(f64_to_bf16_bits(Xc).view(np.int16)).to(dev).view(torch.bfloat16)
+        for _ in range(2):
+            ops.build_transforms(Wd, Xd, wl.G)
+        torch.cuda.synchronize()
+        gpu = []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(5):
+            e0.record()
+            tw, tx, _, _ = ops.build_transforms(Wd, Xd, wl.G)
+            e1.record()
+            torch.cuda.synchronize()
+            gpu.append(e0.elapsed_time(e1))
+        t0 = time.perf_counter()
+        rw, rx = transforms.wush_transforms(torch.from_numpy(W), torch.from_numpy(Xc), wl.G)
+        cpu_ms = (time.perf_counter() - t0) * 1e3
+        dev_err = max(float(((a.cpu() - b).abs().amax(dim=(1, 2)) / b.abs().amax(dim=(1, 2))).max())
+                      for a, b in ((tw, rw), (tx, rx)))
+        print(json.dumps({"workload": name, "d_out": wl.d_out, "n_cal": wl.n_cal, "d_in": wl.K, "G": wl.G,
+                          "blocks": wl.K // wl.G, "gpu_ms": round(statistics.median(gpu), 3),
+                          "torch_cpu_float64_ms": round(cpu_ms, 1), "cpu_threads": torch.get_num_threads(),
+                          "max_rel_diff": float("%.3g" % dev_err)}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -514,6 +560,9 @@ def main():
         return
     if args.layer_loss:
         layer_loss(args)
+        return
+    if args.build_transforms:
+        build_transforms_timing(args)
         return
 
     import numpy as np

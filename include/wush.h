@@ -140,6 +140,28 @@ wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const voi
 wush_status wush_dequant(int fmt, const void* codes, const void* scales, const float* global_scale, int64_t M,
                          int64_t K, float* out, hipStream_t stream);
 
+/* Offline construction of the transforms, on the GPU in float64 ("WUSH",
+ * Eq. 7 and Eq. 8; deep dive, sections 3.2 and 3.4.2-3.4.4).  For every
+ * block c of G input channels:
+ *   Sigma_w = W_c^T W_c / d_out,  Sigma_x = X_c^T X_c / n_cal   (uncentered)
+ *   each + damp * mean(diag) * I;  W', X' = lower Cholesky factors
+ *   W'^T X' = U S V^T (singular values descending; each (u_k, v_k) signed so
+ *   that v_k's largest-magnitude entry is positive, ties to the lowest index)
+ *   T_wush = H S^-1/2 U^T W'^T,  T_xvsh = H S^-1/2 V^T X'^T
+ * with H the Sylvester Hadamard matrix / sqrt(G) (use_hadamard = 1) or I
+ * (use_hadamard = 0, the WUS variant).
+ *   W: bf16 [d_out][d_in] (nn.Linear order); Xcal: bf16 [n_cal][d_in];
+ *   both 16-byte aligned.  G is 16 or 32 and divides d_in; d_out, n_cal >= 1.
+ *   T_wush, T_xvsh: float64 [d_in/G][G][G], 8-byte aligned.
+ *   T_wush_bf16, T_xvsh_bf16: optional (may be NULL) bf16(fp32(T)) copies in
+ *   the kernel layout, 2-byte aligned.
+ *   damp: the relative damping (>= 0; 1e-6 is the reading used elsewhere).
+ * A block whose damped moments are not positive definite (for example all
+ * zero with damp = 0) yields NaN entries.  Errors as for wush_quant. */
+wush_status wush_build_transforms(const void* W, int64_t d_out, const void* Xcal, int64_t n_cal, int64_t d_in,
+                                  int G, double damp, int use_hadamard, double* T_wush, double* T_xvsh,
+                                  void* T_wush_bf16, void* T_xvsh_bf16, hipStream_t stream);
+
 /* Transform only: Y[m][cG+i] = sum_j T[c][i][j] x_(cG+j), in fp32 from the
  * matrix cores, without rounding fix-up.  G is 16 or 32.  Use it to check
  * values before quantization, or when the transformed activations are wanted

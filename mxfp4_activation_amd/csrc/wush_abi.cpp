@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/wush.h"
+#include "wush_build.h"
 #include "wush_dequant.h"
 #include "wush_gemm.h"
 #include "wush_kernels.h"
@@ -323,6 +324,51 @@ wush_status wush_dequant(int fmt, const void* codes, const void* scales, const f
   wush_status st = check_device();
   if (st != WUSH_OK) return st;
   hipError_t e = wush::launch_dequant(fmt, static_cast<const uint8_t*>(codes), scales, global_scale, M, K, out, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+wush_status wush_build_transforms(const void* W, int64_t d_out, const void* Xcal, int64_t n_cal, int64_t d_in,
+                                  int G, double damp, int use_hadamard, double* T_wush, double* T_xvsh,
+                                  void* T_wush_bf16, void* T_xvsh_bf16, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (G != 16 && G != 32) return fail(WUSH_EUNSUPPORTED, "G must be 16 or 32 (got %d)", G);
+  if (d_out < 1 || n_cal < 1) return fail(WUSH_EINVAL, "d_out and n_cal must be >= 1");
+  if (d_in <= 0 || d_in % G != 0) return fail(WUSH_EINVAL, "d_in must be a positive multiple of G");
+  if (d_in / G > 0x7FFFFFFF || d_out > (INT64_MAX / 2) / d_in || n_cal > (INT64_MAX / 2) / d_in)
+    return fail(WUSH_EINVAL, "sizes overflow");
+  if (!(damp >= 0.0)) return fail(WUSH_EINVAL, "damp must be >= 0");
+  if (!W || !Xcal || !T_wush || !T_xvsh) return fail(WUSH_EINVAL, "null pointer");
+  if (!aligned(W, 16) || !aligned(Xcal, 16)) return fail(WUSH_EALIGN, "W and Xcal must be 16-byte aligned");
+  if (!aligned(T_wush, 8) || !aligned(T_xvsh, 8)) return fail(WUSH_EALIGN, "T_wush and T_xvsh must be 8-byte aligned");
+  if ((T_wush_bf16 && !aligned(T_wush_bf16, 2)) || (T_xvsh_bf16 && !aligned(T_xvsh_bf16, 2)))
+    return fail(WUSH_EALIGN, "bf16 outputs must be 2-byte aligned");
+  const uint64_t nt = (uint64_t)d_in * G * 8, nb = (uint64_t)d_in * G * 2;
+  const uint64_t nw = (uint64_t)d_out * d_in * 2, nx = (uint64_t)n_cal * d_in * 2;
+  const void* outs[4] = {T_wush, T_xvsh, T_wush_bf16, T_xvsh_bf16};
+  const uint64_t osz[4] = {nt, nt, nb, nb};
+  for (int i = 0; i < 4; ++i) {
+    if (!outs[i]) continue;
+    if (overlap(outs[i], osz[i], W, nw) || overlap(outs[i], osz[i], Xcal, nx))
+      return fail(WUSH_EINVAL, "an output overlaps an input");
+    for (int j = 0; j < i; ++j)
+      if (outs[j] && overlap(outs[i], osz[i], outs[j], osz[j])) return fail(WUSH_EINVAL, "outputs overlap");
+  }
+  wush_status st = check_device();
+  if (st != WUSH_OK) return st;
+  wush::BuildArgs a{};
+  a.W = static_cast<const uint16_t*>(W);
+  a.X = static_cast<const uint16_t*>(Xcal);
+  a.d_out = d_out;
+  a.n_cal = n_cal;
+  a.d_in = d_in;
+  a.damp = damp;
+  a.use_hadamard = use_hadamard ? 1 : 0;
+  a.T_wush = T_wush;
+  a.T_xvsh = T_xvsh;
+  a.T_wush_bf16 = static_cast<uint16_t*>(T_wush_bf16);
+  a.T_xvsh_bf16 = static_cast<uint16_t*>(T_xvsh_bf16);
+  hipError_t e = wush::launch_build(G, a, stream);
   if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
   return WUSH_OK;
 }

@@ -1,0 +1,23 @@
+// Launcher of the transform construction kernel (wush_build.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wush {
+
+struct BuildArgs {
+  const uint16_t* W;  // bf16 [d_out][d_in]
+  const uint16_t* X;  // bf16 [n_cal][d_in]
+  int64_t d_out, n_cal, d_in;
+  double damp;        // relative damping lam (>= 0)
+  int use_hadamard;   // 1: WUSH, 0: WUS (H = I)
+  double* T_wush;     // [d_in/G][G][G]
+  double* T_xvsh;
+  uint16_t* T_wush_bf16;  // optional bf16(fp32(T)) copies
+  uint16_t* T_xvsh_bf16;
+};
+
+// G is 16 or 32; the caller has validated sizes, alignment and overlap.
+hipError_t launch_build(int G, const BuildArgs& a, hipStream_t s);
+
+}  // namespace wush

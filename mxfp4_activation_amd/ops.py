@@ -79,6 +79,33 @@ def quant_int4(X, T, codes=None, scales=None):
     return quant("int4", X, T, codes=codes, scales=scales)
 
 
+def build_transforms(W: torch.Tensor, Xcal: torch.Tensor, G: int, damp: float = 1e-6, use_hadamard: bool = True,
+                     bf16: bool = True):
+    """WUSH (or WUS) transforms built on the GPU from a bf16 weight [d_out, d_in]
+    and bf16 calibration activations [n_cal, d_in].  Returns (T_wush, T_xvsh)
+    float64 [d_in/G, G, G] and, if bf16, their bf16(fp32(T)) kernel-layout
+    copies (else None)."""
+    for t in (W, Xcal):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError("W and Xcal must be contiguous 2-D bf16 device tensors")
+    d_out, d_in = W.shape
+    n_cal = Xcal.shape[0]
+    if Xcal.shape[1] != d_in:
+        raise ValueError("W and Xcal disagree on d_in")
+    C = d_in // G if G else 0
+    dev = W.device
+    tw = torch.empty((C, G, G), dtype=torch.float64, device=dev)
+    tx = torch.empty((C, G, G), dtype=torch.float64, device=dev)
+    bw = torch.empty((C, G, G), dtype=torch.bfloat16, device=dev) if bf16 else None
+    bx = torch.empty((C, G, G), dtype=torch.bfloat16, device=dev) if bf16 else None
+    lib = _lib.load()
+    _lib.check(lib.wush_build_transforms(W.data_ptr(), d_out, Xcal.data_ptr(), n_cal, d_in, G, float(damp),
+                                         1 if use_hadamard else 0, tw.data_ptr(), tx.data_ptr(),
+                                         bw.data_ptr() if bf16 else None, bx.data_ptr() if bf16 else None, _stream()),
+               "wush_build_transforms")
+    return tw, tx, bw, bx
+
+
 def dequant(fmt: str, codes: torch.Tensor, scales: torch.Tensor, global_scale: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """fp32 values of quantized rows (codes [M][K/2], scales [M][K/G])."""

@@ -115,3 +115,19 @@ def test_dequant_validation_rejects_bad_arguments():
     assert d(0, A, A * 2, None, 4, 64, B + 4) == _lib.WUSH_EALIGN
     assert d(0, A, A * 2, None, 4, 64, A) == _lib.WUSH_EINVAL  # out overlaps codes
     assert d(0, None, A * 2, None, 4, 64, B) == _lib.WUSH_EINVAL
+
+
+def test_build_transforms_validation():
+    lib = wush.load()
+    B = A * 64
+    b = lambda W, do, X, nc, di, G, damp=1e-6, tw=B, tx=B * 2: lib.wush_build_transforms(
+        W, do, X, nc, di, G, damp, 1, tw, tx, None, None, None)
+    assert b(A, 8, A * 2, 8, 64, 24) == _lib.WUSH_EUNSUPPORTED
+    assert b(A, 0, A * 2, 8, 64, 32) == _lib.WUSH_EINVAL
+    assert b(A, 8, A * 2, 0, 64, 32) == _lib.WUSH_EINVAL
+    assert b(A, 8, A * 2, 8, 48, 32) == _lib.WUSH_EINVAL
+    assert b(A, 8, A * 2, 8, 64, 32, damp=-1.0) == _lib.WUSH_EINVAL
+    assert b(A + 8, 8, A * 2, 8, 64, 32) == _lib.WUSH_EALIGN
+    assert b(A, 8, A * 2, 8, 64, 32, tw=B + 4) == _lib.WUSH_EALIGN
+    assert b(A, 8, A * 2, 8, 64, 32, tx=B) == _lib.WUSH_EINVAL  # outputs overlap
+    assert b(None, 8, A * 2, 8, 64, 32) == _lib.WUSH_EINVAL
