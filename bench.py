@@ -97,6 +97,9 @@ def parse():
     ap.add_argument("--build-transforms", action="store_true",
                     help="time the GPU transform construction (wush_build_transforms) against the torch float64 "
                          "builder on each workload's layer, instead of the headline measurement")
+    ap.add_argument("--gptq-wush", action="store_true",
+                    help="GPTQ-WUSH (Algorithm 1) on synthetic 4096-wide layers: calibration time on the GPU and the "
+                         "Eq. 10 output error against RTN, instead of the headline measurement")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="instead of running, read four rocprofv3 --pmc output folders (FETCH_SIZE and "
                          "WRITE_SIZE of the path, then of --copy-probe-mib) and write "
@@ -537,6 +540,54 @@ def build_transforms_timing(args) -> None:
                           "max_rel_diff": float("%.3g" % dev_err)}), flush=True)
 
 
+def gptq_wush_bench(args) -> None:
+    """GPTQ-WUSH (deep dive, section 3.4.6, Algorithm 1) against round-to-
+    nearest on synthetic layers (Student-t(3) activations with 1% outlier
+    channels, N(0, 0.02) weights; 8192 calibration tokens, 2048 held-out
+    tokens).  The weights are calibrated on the device (float64); the
+    held-out tokens then go through the Eq. 10 forward in the kernels (fused
+    transform + MXFP4 quantization, MXFP4 GEMM).  Printed: calibration time
+    and the output error relative to the mean squared exact output, for
+    GPTQ-WUSH, RTN inside Algorithm 1, and RTN with the blockwise Eq. 8
+    transforms."""
+    import numpy as np
+    import torch
+
+    from mxfp4_activation_amd import gptq as pg
+    from mxfp4_activation_amd import ops, transforms
+    from synthetic import f64_to_bf16_bits
+    from synthetic.layers import gen_linear_layer
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    for name, d_in, d_out in (("q_proj-like", 4096, 4096), ("down_proj-like", 12288, 4096)):
+        W, Xc, Xe = gen_linear_layer(d_in, d_out, 8192, 2048, seed=9000 + d_in, n_outlier=d_in // 100)
+        Wd, Xcd = torch.from_numpy(W).to(dev), torch.from_numpy(Xc).to(dev)
+        Xb = torch.from_numpy(f64_to_bf16_bits(Xe).view(np.int16)).to(dev).view(torch.bfloat16)
+        exact = torch.from_numpy(Xe).to(dev) @ Wd.t()
+        den = float((exact ** 2).mean())
+
+        def forward(bank, wc, ws):
+            xc, xs = ops.quant("mxfp4", Xb, bank)
+            out = ops.gemm_mxfp4(xc, xs, wc, ws, out_dtype=torch.float32)
+            return float(((out.double() - exact) ** 2).mean()) / den
+
+        row = {"layer": name, "d_in": d_in, "d_out": d_out, "n_cal": 8192, "n_eval": 2048}
+        for mode in (True, False):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            r = pg.gptq_wush(Wd, Xcd, 32, "mxfp4", gptq=mode)
+            torch.cuda.synchronize()
+            key = "gptq_wush" if mode else "rtn_alg1"
+            row[key + "_calib_s"] = round(time.perf_counter() - t0, 2)
+            row[key + "_rel_err"] = float("%.5g" % forward(transforms.to_kernel_layout(r.T_x.cpu()).to(dev),
+                                                           r.codes, r.scales))
+        Tw, Tx = transforms.wush_transforms(torch.from_numpy(W), torch.from_numpy(Xc), 32)
+        wq_c, wq_s = ops.quant("mxfp4", Wd.to(torch.bfloat16), transforms.to_kernel_layout(Tx).to(dev))
+        row["rtn_eq8_rel_err"] = float("%.5g" % forward(transforms.to_kernel_layout(Tw).to(dev), wq_c, wq_s))
+        print(json.dumps(row), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -563,6 +614,9 @@ def main():
         return
     if args.build_transforms:
         build_transforms_timing(args)
+        return
+    if args.gptq_wush:
+        gptq_wush_bench(args)
         return
 
     import numpy as np

@@ -162,6 +162,29 @@ wush_status wush_build_transforms(const void* W, int64_t d_out, const void* Xcal
                                   int G, double damp, int use_hadamard, double* T_wush, double* T_xvsh,
                                   void* T_wush_bf16, void* T_xvsh_bf16, hipStream_t stream);
 
+/* Intra-block GPTQ step of GPTQ-WUSH ("WUSH", deep dive, section 3.4.6,
+ * Algorithm 1, the GPTQ branch).  One block of transformed weights,
+ *   Wbar: float64 [G][d_out]   (row j = transformed input coordinate j)
+ *   R:    float64 [G][G], the upper Cholesky factor of the inverse block
+ *         Hessian (H S H^T)^-1 (R = I gives round-to-nearest),
+ * is quantized column by column: each output channel o is one group of G
+ * values whose scale comes from their AbsMax (MXFP4: E8M0 code
+ * floor(log2 amax) - 2 + 127; INT4: fp16(fp32(amax) / 7)); for j = 0..G-1,
+ * w_j is quantized at that scale (E2M1 nearest even with saturation, or
+ * INT4 nearest even clamped to +-7) and the error err = (w_j - q_j) / R[j][j]
+ * is spread as w_k -= R[j][k] err for k > j.
+ *   fmt: 0 = MXFP4, 2 = INT4.  G: 16 or 32.
+ *   Q: float64 [G][d_out], the dequantized values.
+ *   codes: row o (G/2 bytes, element 2j in the low nibble) at codes + o *
+ *          codes_stride bytes; 4-byte aligned rows.
+ *   scales: E8M0 byte (MXFP4) or fp16 bits (INT4) of row o at element
+ *           o * scales_stride.
+ * Wbar, R, Q 8-byte aligned; outputs must not overlap inputs.  Errors as for
+ * wush_quant. */
+wush_status wush_gptq_block(int fmt, const double* Wbar, const double* R, int G, int64_t d_out, double* Q,
+                            void* codes, int64_t codes_stride, void* scales, int64_t scales_stride,
+                            hipStream_t stream);
+
 /* Transform only: Y[m][cG+i] = sum_j T[c][i][j] x_(cG+j), in fp32 from the
  * matrix cores, without rounding fix-up.  G is 16 or 32.  Use it to check
  * values before quantization, or when the transformed activations are wanted

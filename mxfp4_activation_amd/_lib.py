@@ -24,6 +24,7 @@ SIGNATURES = {
     "wush_quant": (_c_int, [_c_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "wush_gemm_mxfp4": (_c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _c_int, _vp]),
     "wush_dequant": (_c_int, [_c_int, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "wush_gptq_block": (_c_int, [_c_int, _vp, _vp, _c_int, _i64, _vp, _vp, _i64, _vp, _i64, _vp]),
     "wush_build_transforms": (_c_int, [_vp, _i64, _vp, _i64, _i64, _c_int, ctypes.c_double, _c_int, _vp, _vp, _vp,
                                        _vp, _vp]),
     "wush_transform_f32": (_c_int, [_vp, _vp, _i64, _i64, _c_int, _vp, _vp]),

@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libwush.so")
-SOURCES = ["wush_kernels.hip", "wush_gemm.hip", "wush_dequant.hip", "wush_build.hip", "wush_abi.cpp"]
+SOURCES = ["wush_kernels.hip", "wush_gemm.hip", "wush_dequant.hip", "wush_build.hip", "wush_gptq.hip", "wush_abi.cpp"]
 
 HIPCC_FLAGS = [
     "-O3",

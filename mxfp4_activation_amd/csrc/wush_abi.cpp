@@ -15,6 +15,7 @@
 #include "wush_build.h"
 #include "wush_dequant.h"
 #include "wush_gemm.h"
+#include "wush_gptq.h"
 #include "wush_kernels.h"
 
 namespace {
@@ -369,6 +370,44 @@ wush_status wush_build_transforms(const void* W, int64_t d_out, const void* Xcal
   a.T_wush_bf16 = static_cast<uint16_t*>(T_wush_bf16);
   a.T_xvsh_bf16 = static_cast<uint16_t*>(T_xvsh_bf16);
   hipError_t e = wush::launch_build(G, a, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+wush_status wush_gptq_block(int fmt, const double* Wbar, const double* R, int G, int64_t d_out, double* Q,
+                            void* codes, int64_t codes_stride, void* scales, int64_t scales_stride,
+                            hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (fmt != 0 && fmt != 2) return fail(WUSH_EUNSUPPORTED, "GPTQ block supports MXFP4 (0) and INT4 (2), got %d", fmt);
+  if (G != 16 && G != 32) return fail(WUSH_EUNSUPPORTED, "G must be 16 or 32 (got %d)", G);
+  if (d_out < 0) return fail(WUSH_EINVAL, "d_out must be >= 0");
+  if (d_out == 0) return WUSH_OK;
+  if (d_out > ((int64_t)1 << 40) || codes_stride < G / 2 || scales_stride < 1 || codes_stride > ((int64_t)1 << 40) ||
+      scales_stride > ((int64_t)1 << 40))
+    return fail(WUSH_EINVAL, "bad size or stride");
+  if (!Wbar || !R || !Q || !codes || !scales) return fail(WUSH_EINVAL, "null pointer");
+  if (!aligned(Wbar, 8) || !aligned(R, 8) || !aligned(Q, 8)) return fail(WUSH_EALIGN, "Wbar, R and Q must be 8-byte aligned");
+  if (!aligned(codes, 4) || codes_stride % 4 != 0) return fail(WUSH_EALIGN, "code rows must be 4-byte aligned");
+  if (fmt == 2 && !aligned(scales, 2)) return fail(WUSH_EALIGN, "INT4 scales must be 2-byte aligned");
+  const uint64_t nw = (uint64_t)G * d_out * 8, nr = (uint64_t)G * G * 8;
+  const uint64_t nc = (uint64_t)(d_out - 1) * codes_stride + G / 2;
+  const uint64_t ns = ((uint64_t)(d_out - 1) * scales_stride + 1) * (fmt == 2 ? 2 : 1);
+  if (overlap(Q, nw, Wbar, nw) || overlap(Q, nw, R, nr) || overlap(codes, nc, Wbar, nw) || overlap(codes, nc, R, nr) ||
+      overlap(scales, ns, Wbar, nw) || overlap(scales, ns, R, nr) || overlap(codes, nc, Q, nw) ||
+      overlap(scales, ns, Q, nw))
+    return fail(WUSH_EINVAL, "an output overlaps an input or another output");
+  wush_status st = check_device();
+  if (st != WUSH_OK) return st;
+  wush::GptqArgs a{};
+  a.Wbar = Wbar;
+  a.R = R;
+  a.d_out = d_out;
+  a.Q = Q;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.codes_stride = codes_stride;
+  a.scales = scales;
+  a.scales_stride = scales_stride;
+  hipError_t e = wush::launch_gptq_block(fmt, G, a, stream);
   if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
   return WUSH_OK;
 }

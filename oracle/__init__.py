@@ -21,6 +21,9 @@ Quantization", arXiv 2512.00956):
 * ``gemm``       is the FP4 matrix product that consumes the quantized
   activations and the pre-quantized weights (deep dive, section 3.4.6,
   Eq. 10): decode both MXFP4 operands, multiply in float64.
+* ``gptq``       is GPTQ-WUSH, Algorithm 1 (deep dive, section 3.4.6): the
+  weight side calibrated block by block in reverse order, with the
+  transform rebuilt from the residual target before each block's GPTQ.
 * ``loss``       is the layerwise loss of Eq. 5 (deep dive, section 3.4.1):
   quantize both operands through their block transforms, multiply, and
   take the mean squared error against the unquantized product.

@@ -131,3 +131,17 @@ def test_build_transforms_validation():
     assert b(A, 8, A * 2, 8, 64, 32, tw=B + 4) == _lib.WUSH_EALIGN
     assert b(A, 8, A * 2, 8, 64, 32, tx=B) == _lib.WUSH_EINVAL  # outputs overlap
     assert b(None, 8, A * 2, 8, 64, 32) == _lib.WUSH_EINVAL
+
+
+def test_gptq_block_validation():
+    lib = wush.load()
+    B = A * 64
+    g = lambda fmt, G, d, cs=16, c=B * 3: lib.wush_gptq_block(fmt, A, A * 2, G, d, B, c, cs, B * 5, 1, None)
+    assert g(0, 32, 0) == _lib.WUSH_OK
+    assert g(1, 32, 8) == _lib.WUSH_EUNSUPPORTED  # NVFP4 not offered
+    assert g(0, 24, 8) == _lib.WUSH_EUNSUPPORTED
+    assert g(0, 32, -1) == _lib.WUSH_EINVAL
+    assert g(0, 32, 8, cs=8) == _lib.WUSH_EINVAL  # row stride shorter than a group's bytes
+    assert g(0, 32, 8, cs=18) == _lib.WUSH_EALIGN
+    assert g(0, 32, 8, c=B * 3 + 2) == _lib.WUSH_EALIGN
+    assert g(0, 32, 8, c=B) == _lib.WUSH_EINVAL  # codes overlap Q
