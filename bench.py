@@ -820,9 +820,16 @@ def _kernel_source_sha() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in ("wush_kernels.hip", "wush_kernels.h", "wush_abi.cpp"):
-        with open(os.path.join(ROOT, "mxfp4_activation_amd", "csrc", name), "rb") as f:
+    # The quantization kernel's sources and its launch planner (plan_quant in
+    # the ABI file); the other entry points of the library do not enter.
+    csrc = os.path.join(ROOT, "mxfp4_activation_amd", "csrc")
+    for name in ("wush_kernels.hip", "wush_kernels.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(csrc, "wush_abi.cpp"), "rb") as f:
+        abi = f.read()
+    start = abi.find(b"void plan_quant(")
+    h.update(abi[start:abi.find(b"\n}\n", start) + 3] if start >= 0 else abi)
     return h.hexdigest()[:16]
 
 
