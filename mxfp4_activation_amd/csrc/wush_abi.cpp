@@ -196,18 +196,17 @@ wush_status wush_quant_int4(const void* X, const void* T, int64_t M, int64_t K, 
 }
 
 static wush_status transform_common(const void* X, const void* T, int64_t M, int64_t K, int G,
-                                    float* Y, uint32_t* amax_bits, hipStream_t stream) {
+                                    float* Y, hipStream_t stream) {
   wush::TransformArgs a{};
   a.X = static_cast<const uint16_t*>(X);
   a.T = static_cast<const uint16_t*>(T);
   a.Y = Y;
-  a.amax_bits = amax_bits;
   a.M = M;
   a.K = K;
   plan(M, K, &a.n_tiles, &a.tiles_per_wave, &a.n_panels, &a.n_pg, &a.n_tg);
   const int64_t n_wg = (int64_t)a.n_pg * a.n_tg;
   if (n_wg > 0x7FFFFFFF) return fail(WUSH_EINVAL, "problem too large for one launch");
-  hipError_t e = wush::launch_transform(G, amax_bits != nullptr, a, (int)n_wg, stream);
+  hipError_t e = wush::launch_transform(G, a, (int)n_wg, stream);
   if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
   return WUSH_OK;
 }
@@ -223,9 +222,12 @@ wush_status wush_transform_f32(const void* X, const void* T, int64_t M, int64_t 
     return fail(WUSH_EINVAL, "Y overlaps an input");
   st = check_device();
   if (st != WUSH_OK) return st;
-  return transform_common(X, T, M, K, G, Y, nullptr, stream);
+  return transform_common(X, T, M, K, G, Y, stream);
 }
 
+// The AbsMax pre-pass runs the quant kernel's tiling (same planner), so it
+// streams X in the same row-contiguous pattern.  M = 0 launches only the
+// fill, which writes the empty tensor's AbsMax, 0.
 static wush_status absmax_common(const void* X, const void* T, int64_t M, int64_t K, int G, float* out,
                                  hipStream_t stream) {
   wush_status st = check_shape(X, T, M, K, G);
@@ -236,17 +238,23 @@ static wush_status absmax_common(const void* X, const void* T, int64_t M, int64_
     return fail(WUSH_EINVAL, "output overlaps an input");
   st = check_device();
   if (st != WUSH_OK) return st;
-  if (M == 0) {
-    // The AbsMax of an empty tensor is 0.  Write it with the same fill
-    // kernel the non-empty path uses.
-    wush::TransformArgs a{};
-    a.amax_bits = reinterpret_cast<uint32_t*>(out);
-    a.K = K;
-    hipError_t e = wush::launch_transform(G, true, a, 0, stream);
-    (void)e;
-    return WUSH_OK;
+  wush::QuantArgs a{};
+  a.X = static_cast<const uint16_t*>(X);
+  a.T = static_cast<const uint16_t*>(T);
+  a.amax_bits = reinterpret_cast<uint32_t*>(out);
+  a.M = M;
+  a.K = K;
+  int64_t n_wg = 0;
+  if (M > 0) {
+    plan_quant(M, K, &a.n_tiles, &a.tiles_per_wave, &a.n_panels, &a.n_pg, &a.n_tg);
+    n_wg = (int64_t)a.n_pg * a.n_tg;
+    if (n_wg > 0x7FFFFFFF) return fail(WUSH_EINVAL, "problem too large for one launch");
+  } else {
+    a.tiles_per_wave = 1;
   }
-  return transform_common(X, T, M, K, G, nullptr, reinterpret_cast<uint32_t*>(out), stream);
+  hipError_t e = wush::launch_absmax(G, a, (int)n_wg, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
 }
 
 wush_status wush_transformed_absmax(const void* X, const void* T, int64_t M, int64_t K, int G,

@@ -26,6 +26,7 @@ struct QuantArgs {
   uint8_t* scales;
   const float* global_scale;
   uint32_t* n_exact;
+  uint32_t* amax_bits;     // AbsMax kernel only: running max |y| as bits
   int64_t M;
   int64_t K;
   int64_t n_tiles;         // ceil(M / 32)
@@ -39,7 +40,6 @@ struct TransformArgs {
   const uint16_t* X;
   const uint16_t* T;
   float* Y;
-  uint32_t* amax_bits;
   int64_t M;
   int64_t K;
   int64_t n_tiles;
@@ -50,7 +50,9 @@ struct TransformArgs {
 };
 
 hipError_t launch_quant(int fmt, const QuantArgs& a, int n_wg, hipStream_t s);
-hipError_t launch_transform(int G, bool absmax, const TransformArgs& a, int n_wg, hipStream_t s);
+hipError_t launch_transform(int G, const TransformArgs& a, int n_wg, hipStream_t s);
+// Writes 0 to a.amax_bits, then folds max |T x| over the tensor into it.
+hipError_t launch_absmax(int G, const QuantArgs& a, int n_wg, hipStream_t s);
 hipError_t launch_global_scale(float* out, hipStream_t s);
 hipError_t launch_e2m1(const float* v, int64_t n, uint8_t* out, hipStream_t s);
 

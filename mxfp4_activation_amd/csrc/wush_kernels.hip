@@ -525,7 +525,12 @@ __device__ __forceinline__ void panel_step(uint8_t* row, float* ybuf, const Frag
 // 2^26, so every tile is complete, every scale row segment is 8- or 16-byte
 // aligned, and per-lane offsets fit in 32 bits.  Addresses are then a
 // uniform per-tile base (scalar registers) plus a per-lane offset.
-template <int FMT, int TPW, bool FULL>
+//
+// AMAX: the same run computes only max |y| over its tiles (the NVFP4
+// per-tensor AbsMax pre-pass) and folds it into *a.amax_bits.  Rows past M
+// repeat row M - 1 and channels past K are zero on both sides, so they
+// change no maximum.
+template <int FMT, int TPW, bool FULL, bool AMAX = false>
 __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, int cg, int tg) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   const int tid = threadIdx.x;
@@ -572,7 +577,7 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
   u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
   asm volatile("" : "+v"(ones));  // materialized once, kept in VGPRs
   float g = 0.0f;
-  if (FMT == kNVFP4) g = *a.global_scale;
+  if (FMT == kNVFP4 && !AMAX) g = *a.global_scale;
 
   // 2. stage, in arrival order
 #pragma unroll
@@ -581,6 +586,41 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
     *reinterpret_cast<u32x4*>(L.xs[u] + (row_a + 16) * kXRow + 16 * chunk) = v[u][1];
   }
   __syncthreads();
+
+  if (AMAX) {
+    // 3'. contract; the run's max |y|, one atomic per workgroup at most.
+    float m = 0.0f;
+    if (panel_ok) {
+      const uint8_t* row = L.xs[0] + (lane & 31) * kXRow + wave * 64 + 16 * (lane >> 5);
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        if (!FULL && u >= n_tiles) break;
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(row + u * (32 * kXRow));
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(row + u * (32 * kXRow) + 32);
+        f32x16 zero = {};
+        f32x16 acc = mfma32(f.t0, b0, zero);
+        acc = mfma32(f.t1, b1, acc);
+        m = fmaxf(m, max_abs16(acc));
+      }
+    }
+    uint32_t mb = __float_as_uint(m);  // non-negative floats order like their bit patterns
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint32_t v = (uint32_t)__shfl_xor((int)mb, o, 64);
+      mb = mb > v ? mb : v;
+    }
+    uint32_t* red = reinterpret_cast<uint32_t*>(L.y[0]);
+    if (lane == 0) red[wave] = mb;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t w = red[0];
+      for (int i = 1; i < kQWaves; ++i) w = w > red[i] ? w : red[i];
+      // The stored value only grows, so a stale read just costs an atomic.
+      if (w > __hip_atomic_load(a.amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        atomicMax(a.amax_bits, w);
+    }
+    return;
+  }
 
   // 3. contract and quantize
   uint32_t n_exact = 0;
@@ -667,9 +707,22 @@ __global__ __launch_bounds__(kQWaves * 64, (FMT == kMXFP4) ? 8 : 1) void quant_k
   else quant_run<FMT, TPW, false>(a, L, cg, tg);
 }
 
-// ---------------------------------------------------------------- transform / absmax
+// The tensor AbsMax of the transformed activations (NVFP4's per-tensor
+// scale), in the quant kernel's run structure: FMT kMXFP4 for G = 32,
+// kNVFP4 for G = 16.
+template <int FMT, int TPW>
+__global__ __launch_bounds__(kQWaves * 64) void absmax_kernel(QuantArgs a) {
+  __shared__ __attribute__((aligned(16))) QuantLds<TPW> L;
+  int cg, tg;
+  wg_coords(a.n_pg, a.n_tg, cg, tg);
+  const bool full = ((int64_t)(tg + 1) * TPW * 32 <= a.M) && (a.K % (kPanels * 32) == 0) && a.K <= (1 << 26);
+  if (full) quant_run<FMT, TPW, true, true>(a, L, cg, tg);
+  else quant_run<FMT, TPW, false, true>(a, L, cg, tg);
+}
 
-template <int G, bool ABSMAX>
+// ---------------------------------------------------------------- transform
+
+template <int G>
 __global__ __launch_bounds__(kWaves * 64) void transform_kernel(TransformArgs a) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -686,7 +739,6 @@ __global__ __launch_bounds__(kWaves * 64) void transform_kernel(TransformArgs a)
   const bool group_ok = (G == 32) || (2 * p + h < C);
   const int64_t tile0 = (int64_t)tg * a.tiles_per_wave;
   const int64_t tile1 = (tile0 + a.tiles_per_wave < a.n_tiles) ? tile0 + a.tiles_per_wave : a.n_tiles;
-  float wmax = 0.0f;
   for (int64_t t = tile0; t < tile1; ++t) {
     const int64_t m = t * 32 + n;
     const uint16_t* src = a.X + (m < a.M ? m : a.M - 1) * a.K + c_in;
@@ -697,9 +749,7 @@ __global__ __launch_bounds__(kWaves * 64) void transform_kernel(TransformArgs a)
     f32x16 acc = mfma32(f.t0, x.b0, zero);
     acc = mfma32(f.t1, x.b1, acc);
     if (m >= a.M) continue;
-    if (ABSMAX) {
-      if (group_ok) wmax = fmaxf(wmax, max_abs16(acc));
-    } else if (group_ok) {
+    if (group_ok) {
       f32x4* dst = reinterpret_cast<f32x4*>(a.Y + m * a.K + out0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -707,11 +757,6 @@ __global__ __launch_bounds__(kWaves * 64) void transform_kernel(TransformArgs a)
         __builtin_nontemporal_store(v, &dst[q]);
       }
     }
-  }
-  if (ABSMAX) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) wmax = fmaxf(wmax, __shfl_xor(wmax, o, 64));
-    if (lane == 0) atomicMax(a.amax_bits, __float_as_uint(wmax));  // non-negative floats order as uints
   }
 }
 
@@ -760,17 +805,29 @@ hipError_t launch_quant(int fmt, const QuantArgs& a, int n_wg, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_transform(int G, bool absmax, const TransformArgs& a, int n_wg, hipStream_t s) {
+hipError_t launch_transform(int G, const TransformArgs& a, int n_wg, hipStream_t s) {
   dim3 grid(n_wg), block(kWaves * 64);
-  if (absmax) {
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(1), 0, s, a.amax_bits, 0u);
-    if (n_wg == 0) return hipGetLastError();
-    if (G == 32) hipLaunchKernelGGL((transform_kernel<32, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((transform_kernel<16, true>), grid, block, 0, s, a);
-  } else {
-    if (G == 32) hipLaunchKernelGGL((transform_kernel<32, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((transform_kernel<16, false>), grid, block, 0, s, a);
+  if (G == 32) hipLaunchKernelGGL((transform_kernel<32>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((transform_kernel<16>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static void launch_absmax_fmt(const QuantArgs& a, int n_wg, hipStream_t s) {
+  dim3 grid(n_wg), block(kQWaves * 64);
+  switch (a.tiles_per_wave) {
+    case 1: hipLaunchKernelGGL((absmax_kernel<FMT, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((absmax_kernel<FMT, 2>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((absmax_kernel<FMT, 4>), grid, block, 0, s, a); break;
   }
+}
+
+hipError_t launch_absmax(int G, const QuantArgs& a, int n_wg, hipStream_t s) {
+  if (a.tiles_per_wave != 1 && a.tiles_per_wave != 2 && a.tiles_per_wave != 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(1), 0, s, a.amax_bits, 0u);
+  if (n_wg == 0) return hipGetLastError();
+  if (G == 32) launch_absmax_fmt<kMXFP4>(a, n_wg, s);
+  else launch_absmax_fmt<kNVFP4>(a, n_wg, s);
   return hipGetLastError();
 }
 

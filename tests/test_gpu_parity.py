@@ -269,18 +269,60 @@ def test_transform_f32_error_bounds(G):
     print("G=%d relative error vs float64 T: median %.2e, max %.2e" % (G, np.median(rel), rel.max()))
 
 
-def test_absmax_and_global_scale():
+@pytest.mark.parametrize("G,rows,blocks", [
+    (16, None, None),   # the whole tiny tensor
+    (32, None, None),
+    (16, 77, 3),        # ragged: M not a multiple of 32, K = 48 (not a multiple of 256)
+    (32, 45, 3),        # K = 96
+    (32, 200, 5),       # several tiles, K = 160
+])
+def test_absmax_and_global_scale(G, rows, blocks):
     from mxfp4_activation_amd import ops
 
-    _, tb = cases.transforms("tiny_mxfp4", 16)
+    _, tb = cases.transforms("tiny_mxfp4", G)
     xb = cases.x_full("tiny_mxfp4")
+    if rows is not None:
+        xb = np.ascontiguousarray(xb[:rows, : blocks * G])
+        tb = np.ascontiguousarray(tb[:blocks])
     y, A = quant.transform_ref(xb, tb, return_abs=True)
     X, T = _dev_bf16(xb), _dev_bf16(tb)
     amax = float(ops.transformed_absmax(X, T).item())
     ref = float(quant.tensor_amax_ref(y))
     assert abs(amax - ref) <= (2.0 ** -17) * A.max() + (2.0 ** -21) * ref
+    if G == 16:
+        g = float(ops.nvfp4_global_scale(X, T).item())
+        assert g == float(np.float32(np.float32(amax) / np.float32(2688.0)))
+
+
+def test_absmax_empty_is_zero():
+    from mxfp4_activation_amd import ops
+
+    _, tb = cases.transforms("tiny_mxfp4", 16)
+    X = torch.empty((0, tb.shape[0] * 16), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    ops.transformed_absmax(X, _dev_bf16(tb), out=out)
+    assert float(out.item()) == 0.0
+
+
+def test_global_scale_full_nvfp4_workload():
+    """The AbsMax pre-pass over the whole 16384 x 4096 NVFP4 tensor against
+    the oracle's.  Bound: the fp32 accumulation error of one output,
+    2^-17 * sum_j |T_kj x_j| (bounded by the largest row L1 norm of |T|
+    times max |x|), plus the final rounding."""
+    from mxfp4_activation_amd import ops
+
+    _, tb = cases.transforms("nvfp4")
+    xb = cases.x_full("nvfp4")
+    X, T = _dev_bf16(xb), _dev_bf16(tb)
+    amax = float(ops.transformed_absmax(X, T).item())
     g = float(ops.nvfp4_global_scale(X, T).item())
+    g_ref = float(cases.oracle_global_scale("nvfp4"))
+    ref = g_ref * 2688.0
+    t_l1 = np.abs(codecs.bf16_bits_to_f32(tb).astype(np.float64)).sum(axis=2).max()
+    x_max = np.abs(codecs.bf16_bits_to_f32(xb)).max()
+    assert abs(amax - ref) <= (2.0 ** -17) * t_l1 * x_max + (2.0 ** -20) * ref, (amax, ref)
     assert g == float(np.float32(np.float32(amax) / np.float32(2688.0)))
+    print("AbsMax %.9g, oracle %.9g, g %.9g, oracle g %.9g" % (amax, ref, g, g_ref))
 
 
 def test_deterministic_and_in_bounds():
