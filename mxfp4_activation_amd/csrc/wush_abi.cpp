@@ -89,17 +89,21 @@ void plan(int64_t M, int64_t K, int64_t* n_tiles, int64_t* tpw, int* n_panels, i
 }
 
 // Quant kernel split: a workgroup (8 waves) owns a 256-channel column of
-// the input and a run of TPW 32-token tiles, all loaded at entry.  TPW
-// (1, 2 or 4) is the longest run that still gives at least 1024 workgroups
-// (four per CU), so that several workgroups share each CU and cover each
-// other's waits; longer runs amortize the T fragment loads on big batches.
-// WUSH_TILES_PER_WG overrides it for tuning.
-void plan_quant(int64_t M, int64_t K, int64_t* n_tiles, int64_t* tpw, int* n_panels, int* n_pg, int* n_tg) {
+// the input and a run of TPW 32-token tiles, all loaded at entry.  TPW is
+// the longest run up to a per-format cap that still gives at least 1024
+// workgroups (four per CU), so that several workgroups share each CU and
+// cover each other's waits.  The cap is 2 for MXFP4 and NVFP4: longer runs
+// need twice the LDS per workgroup (two per CU instead of four), which
+// measured slower on every large batch.  INT4 does twice the vector work per
+// tile and is compute-bound; for it 4 tiles measured faster than 2.
+// WUSH_TILES_PER_WG overrides the choice for tuning.
+void plan_quant(int fmt, int64_t M, int64_t K, int64_t* n_tiles, int64_t* tpw, int* n_panels, int* n_pg,
+                int* n_tg) {
   *n_tiles = (M + 31) / 32;
   *n_panels = (int)((K + 31) / 32);
   *n_pg = (*n_panels + wush::kPanelsPerTile - 1) / wush::kPanelsPerTile;
   const int64_t target_wg = 8192 / wush::kPanelsPerTile;  // 4 eight-wave workgroups per CU
-  int64_t t = 4;
+  int64_t t = fmt == wush::kINT4 ? 4 : 2;
   while (t > 1 && (int64_t)(*n_pg) * ((*n_tiles + t - 1) / t) < target_wg) t >>= 1;
   static const int64_t env = [] {
     const char* s = getenv("WUSH_TILES_PER_WG");
@@ -171,7 +175,7 @@ wush_status wush_quant(int fmt, const void* X, const void* T, int64_t M, int64_t
   a.n_exact = n_exact;
   a.M = M;
   a.K = K;
-  plan_quant(M, K, &a.n_tiles, &a.tiles_per_wave, &a.n_panels, &a.n_pg, &a.n_tg);
+  plan_quant(fmt, M, K, &a.n_tiles, &a.tiles_per_wave, &a.n_panels, &a.n_pg, &a.n_tg);
   const int64_t n_wg = (int64_t)a.n_pg * a.n_tg;
   if (n_wg > 0x7FFFFFFF) return fail(WUSH_EINVAL, "problem too large for one launch");
   hipError_t e = wush::launch_quant(fmt, a, (int)n_wg, stream);
@@ -246,7 +250,7 @@ static wush_status absmax_common(const void* X, const void* T, int64_t M, int64_
   a.K = K;
   int64_t n_wg = 0;
   if (M > 0) {
-    plan_quant(M, K, &a.n_tiles, &a.tiles_per_wave, &a.n_panels, &a.n_pg, &a.n_tg);
+    plan_quant(G == 16 ? wush::kNVFP4 : wush::kMXFP4, M, K, &a.n_tiles, &a.tiles_per_wave, &a.n_panels, &a.n_pg, &a.n_tg);
     n_wg = (int64_t)a.n_pg * a.n_tg;
     if (n_wg > 0x7FFFFFFF) return fail(WUSH_EINVAL, "problem too large for one launch");
   } else {

@@ -147,8 +147,8 @@ __device__ __forceinline__ bool mx_unsure(float amax, float d) {
   return e8m0_code(fmaxf(amax - d, 0.0f)) != e8m0_code(amax + d);
 }
 
-__device__ __forceinline__ bool int4_unsure(float amax, float d) {
-  float q = amax / 7.0f;
+// q = fp32(amax / 7), the value the fp16 scale rounds.
+__device__ __forceinline__ bool int4_unsure(float q, float d) {
   float dq = d * 0.15f + q * 0x1p-21f;
   return f16_bits(fmaxf(q - dq, 0.0f)) != f16_bits(q + dq);
 }
@@ -347,12 +347,14 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
   if (G == 32) amax = max_halves(amax);
   const float d = err_bound(bound, bound_scale, amax);
   bool unsure;
+  float q7 = 0.0f;  // INT4: fp32(amax / 7), computed once per decision
   if (FMT == kMXFP4) {
     // The E8M0 code depends only on the exponent field of amax.  It is
     // settled when amax - d and amax + d share sign and exponent field.
     unsure = (__float_as_uint(amax - d) ^ __float_as_uint(amax + d)) > 0x007FFFFFu;
   } else if (FMT == kINT4) {
-    unsure = int4_unsure(amax, d);
+    q7 = amax / 7.0f;
+    unsure = int4_unsure(q7, d);
   } else {
     unsure = nv_unsure(amax, d, g);
   }
@@ -366,6 +368,7 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
     }
     amax = max_abs16(acc);
     if (G == 32) amax = max_halves(amax);
+    if (FMT == kINT4) q7 = amax / 7.0f;
   }
   if (FMT == kMXFP4) {
     // 2^e with e = floor(log2 amax) - 2, clamped at 2^-127 (code 0): the
@@ -375,7 +378,7 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
     scale_bits = sc >> 23;
     return pack_e2m1(acc, __uint_as_float(sc));
   } else if (FMT == kINT4) {
-    uint32_t sb = f16_bits(amax / 7.0f);
+    uint32_t sb = f16_bits(q7);
     float s = f16_value(sb);
     scale_bits = sb;
     return pack_int4(acc, s > 0.0f ? 1.0f / s : 0.0f);
