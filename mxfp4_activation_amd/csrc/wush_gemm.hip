@@ -14,21 +14,22 @@
 // the low nibble of byte t) and that block's E8M0 scale byte, which is
 // exactly the row-major layout the quantization kernel writes.
 //
-// Workgroup: a 128 x 128 tile of C and 8 waves in two groups of 4.  K runs
-// in steps of 256 elements (128 code bytes per row); group g takes the
-// second half-range [128 g, 128 g + 128) of every step (the K sum is split
+// Workgroup: a 64 TM x 64 TM tile of C (TM = 2: 128 x 128; TM = 1, for
+// grids that would leave CUs idle: 64 x 64) and 8 waves in two groups of 4.
+// K runs in steps of 256 elements (128 code bytes per row); group g takes
+// the half-range [128 g, 128 g + 128) of every step (the K sum is split
 // inside the workgroup) and the two partial tiles are added through LDS at
 // the end.  Every SIMD holds one wave of each group.  Within a group, wave
-// (wm, wn) owns a 64 x 64 quarter: 2 x 2 MFMA tiles of 32 x 32.
+// (wm, wn) owns a quarter: TM x TM MFMA tiles of 32 x 32.
 //
 // Operands go from global memory straight into LDS (global_load_lds, 16 B
-// per lane, whole 128-byte rows), through a ring of 4 step stages, two
-// steps ahead of the MFMAs.  No staging registers and no LDS write
+// per lane, whole 128-byte rows), through a ring of step stages (4 at
+// TM = 2, 8 at TM = 1), 2 or 4 steps ahead of the MFMAs.  No staging registers and no LDS write
 // instructions are involved; each wave waits for its own loads with vmcnt
 // and one barrier per step publishes them.
 //
-// LDS layout of a stage: A codes [128 rows][128 B], B codes [128][128 B], A
-// scales [128][8 B], B scales [128][8 B].  A load instruction writes 1 KB
+// LDS layout of a stage (BT = 64 TM rows): A codes [BT rows][128 B], B
+// codes [BT][128 B], A scales [BT][8 B], B scales [BT][8 B].  A load instruction writes 1 KB
 // contiguously (8 rows), so rows are not padded: the 16-byte chunk c of
 // row r sits in slot c ^ ((r >> 1) & 7) instead, which gives the operand
 // reads of 16 consecutive rows 16 distinct bank groups.  Sub-step s of a
