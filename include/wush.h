@@ -193,8 +193,12 @@ wush_status wush_gptq_block(int fmt, const double* Wbar, const double* R, int G,
 wush_status wush_transform_f32(const void* X, const void* T, int64_t M, int64_t K, int G,
                                float* Y, hipStream_t stream);
 
-/* Largest |y| over the whole transformed tensor (fp32, matrix-core values).
- * *amax is overwritten, not accumulated.  G is 16 or 32. */
+/* Largest |y| over the whole transformed tensor (fp32, matrix-core values:
+ * within 2^-17 * max_k sum_j |T_kj x_j| + 2^-21 * amax of the exact
+ * maximum).  *amax is overwritten, not accumulated: the call enqueues a
+ * fill of *amax with 0, then the pass, which folds each workgroup's maximum
+ * in with an atomic max.  Two calls that share `amax` on different streams
+ * race.  G is 16 or 32. */
 wush_status wush_transformed_absmax(const void* X, const void* T, int64_t M, int64_t K, int G,
                                     float* amax, hipStream_t stream);
 
