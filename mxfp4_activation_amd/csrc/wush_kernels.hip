@@ -140,26 +140,33 @@ __device__ __forceinline__ float f16_value(uint32_t b) {
 
 // ---------------------------------------------------------------- scale decisions
 //
-// Each decision is a monotone function of amax.  `unsure` reports whether it
-// could change anywhere in [amax - d, amax + d].
+// Each decision is a monotone function of amax.  The checks report whether
+// it could change anywhere in [amax - d, amax + d].  When it cannot, the
+// decision at the top of the interval (returned through the reference) is
+// the decision at amax itself, so the caller reuses it.
 
 __device__ __forceinline__ bool mx_unsure(float amax, float d) {
   return e8m0_code(fmaxf(amax - d, 0.0f)) != e8m0_code(amax + d);
 }
 
-// q = fp32(amax / 7), the value the fp16 scale rounds.
-__device__ __forceinline__ bool int4_unsure(float q, float d) {
+// INT4: q = fp32(amax / 7), the value the fp16 scale rounds; `bits` gets
+// the fp16 scale.
+__device__ __forceinline__ bool int4_unsure(float q, float d, uint32_t& bits) {
   float dq = d * 0.15f + q * 0x1p-21f;
-  return f16_bits(fmaxf(q - dq, 0.0f)) != f16_bits(q + dq);
+  bits = f16_bits(q + dq);
+  return f16_bits(fmaxf(q - dq, 0.0f)) != bits;
 }
 
-__device__ __forceinline__ bool nv_unsure(float amax, float d, float g) {
+// NVFP4: the E4M3 code of fp32(fp32(amax / 6) / g) goes to `code`.
+__device__ __forceinline__ bool nv_unsure(float amax, float d, float g, uint32_t& code) {
+  code = 0u;
   if (!(g > 0.0f)) return false;  // every code is zero whatever amax is
-  float ratio = (amax / 6.0f) / g;
   if (amax == 0.0f) return d > 0.0f && e4m3_code((d / 6.0f) / g) != 0u;
+  const float ratio = (amax / 6.0f) / g;
   // ratio scales linearly with amax; the relative slack covers roundings
-  float dr = ratio * (d * __builtin_amdgcn_rcpf(amax)) * 1.01f + ratio * 0x1p-20f;
-  return e4m3_code(fmaxf(ratio - dr, 0.0f)) != e4m3_code(ratio + dr);
+  const float dr = ratio * (d * __builtin_amdgcn_rcpf(amax)) * 1.01f + ratio * 0x1p-20f;
+  code = e4m3_code(ratio + dr);
+  return e4m3_code(fmaxf(ratio - dr, 0.0f)) != code;
 }
 
 // ---------------------------------------------------------------- fragments
@@ -347,16 +354,15 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
   if (G == 32) amax = max_halves(amax);
   const float d = err_bound(bound, bound_scale, amax);
   bool unsure;
-  float q7 = 0.0f;  // INT4: fp32(amax / 7), computed once per decision
+  uint32_t sdec = 0u;  // INT4 / NVFP4: the settled scale bits
   if (FMT == kMXFP4) {
     // The E8M0 code depends only on the exponent field of amax.  It is
     // settled when amax - d and amax + d share sign and exponent field.
     unsure = (__float_as_uint(amax - d) ^ __float_as_uint(amax + d)) > 0x007FFFFFu;
   } else if (FMT == kINT4) {
-    q7 = amax / 7.0f;
-    unsure = int4_unsure(q7, d);
+    unsure = int4_unsure(amax / 7.0f, d, sdec);
   } else {
-    unsure = nv_unsure(amax, d, g);
+    unsure = nv_unsure(amax, d, g, sdec);
   }
   uint64_t pending = __ballot(unsure);
   if (pending) {
@@ -368,7 +374,10 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
     }
     amax = max_abs16(acc);
     if (G == 32) amax = max_halves(amax);
-    if (FMT == kINT4) q7 = amax / 7.0f;
+    // Decide again at the new amax (the same value for the groups that were
+    // not recomputed).
+    if (FMT == kINT4) sdec = f16_bits(amax / 7.0f);
+    if (FMT == kNVFP4 && g > 0.0f) sdec = e4m3_code((amax / 6.0f) / g);
   }
   if (FMT == kMXFP4) {
     // 2^e with e = floor(log2 amax) - 2, clamped at 2^-127 (code 0): the
@@ -378,15 +387,13 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
     scale_bits = sc >> 23;
     return pack_e2m1(acc, __uint_as_float(sc));
   } else if (FMT == kINT4) {
-    uint32_t sb = f16_bits(q7);
-    float s = f16_value(sb);
-    scale_bits = sb;
+    const float s = f16_value(sdec);
+    scale_bits = sdec;
     return pack_int4(acc, s > 0.0f ? 1.0f / s : 0.0f);
   } else {
-    uint32_t code = 0;
+    const uint32_t code = sdec;  // 0 when g <= 0
     float r = 0.0f;
     if (g > 0.0f) {
-      code = e4m3_code((amax / 6.0f) / g);
       float eff = e4m3_value(code) * g;
       r = eff > 0.0f ? 1.0f / eff : 0.0f;
     }
