@@ -201,7 +201,7 @@ __device__ __forceinline__ Frag load_t(const uint16_t* __restrict__ T, int p, in
       else f.t1 = t;
     }
   }
-  f.a0 = z;  // |T| is filled in by with_abs() once the loads are in flight
+  f.a0 = z;  // |T|: with_abs() fills it in where the bound needs it
   f.a1 = z;
   return f;
 }
@@ -287,19 +287,23 @@ __device__ __forceinline__ u32x2 pack_e2m1(const f32x16& v, float scale) {
 
 // INT4 element: rne(clamp(y * r, -7, 7)) as a two's-complement nibble.  After
 // adding 1.5 * 2^23, the low mantissa bits of the fp32 sum hold the rounded
-// integer.
+// integer.  CLAMP = false skips the clamp where it cannot change the
+// result (see quantize_panel).
+template <bool CLAMP>
 __device__ __forceinline__ uint32_t int4_bits(float y, float r) {
-  float v = fminf(fmaxf(y * r, -7.0f), 7.0f);
+  float v = y * r;
+  if (CLAMP) v = fminf(fmaxf(v, -7.0f), 7.0f);
   return __float_as_uint(v + 12582912.0f);
 }
 
 // Pack 16 INT4 values: v_perm_b32 gathers the low byte of four results into
 // one word (even elements in one word, odd in the other).  Then the two words
 // merge as nibble pairs.
+template <bool CLAMP>
 __device__ __forceinline__ uint32_t pack_int4x8(const f32x16& v, int base, float r) {
   uint32_t q[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) q[k] = int4_bits(v[base + k], r);
+  for (int k = 0; k < 8; ++k) q[k] = int4_bits<CLAMP>(v[base + k], r);
   // bytes {q0, q2, q4, q6} and {q1, q3, q5, q7}
   uint32_t e01 = __builtin_amdgcn_perm(q[2], q[0], 0x0c0c0400u);  // [q0.b0, q2.b0, 0, 0]
   uint32_t e23 = __builtin_amdgcn_perm(q[6], q[4], 0x04000c0cu);  // [0, 0, q4.b0, q6.b0]
@@ -310,8 +314,9 @@ __device__ __forceinline__ uint32_t pack_int4x8(const f32x16& v, int base, float
   return ev | (od << 4);
 }
 
+template <bool CLAMP>
 __device__ __forceinline__ u32x2 pack_int4(const f32x16& v, float r) {
-  u32x2 w = {pack_int4x8(v, 0, r), pack_int4x8(v, 8, r)};
+  u32x2 w = {pack_int4x8<CLAMP>(v, 0, r), pack_int4x8<CLAMP>(v, 8, r)};
   return w;
 }
 
@@ -389,7 +394,14 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
   } else if (FMT == kINT4) {
     const float s = f16_value(sdec);
     scale_bits = sdec;
-    return pack_int4(acc, s > 0.0f ? 1.0f / s : 0.0f);
+    const float r = s > 0.0f ? 1.0f / s : 0.0f;
+    // With a normal fp16 scale, |y| <= amax and s >= fp32(amax / 7) (1 -
+    // 2^-11) give |y r| <= 7.0035 after the roundings of r and of the
+    // product: below 7.5, so rounding already lands in [-7, 7].  Zero and
+    // subnormal scales (tiny amax) need the clamp; an infinite scale gives
+    // r = 0.  The branch is taken per wave.
+    if (__ballot((sdec & 0x7C00u) == 0u)) return pack_int4<true>(acc, r);
+    return pack_int4<false>(acc, r);
   } else {
     const uint32_t code = sdec;  // 0 when g <= 0
     float r = 0.0f;
@@ -512,8 +524,8 @@ __device__ __forceinline__ void panel_step(uint8_t* row, float* ybuf, const Frag
                                                  __builtin_bit_cast(bf16x8, x.b1 & mask), l1, 0, 0, 0);
     bound = l1[0];
   } else {
-    f32x16 aab = mfma32(f.t0 & mask, x.b0 & mask, zero);
-    aab = mfma32(f.t1 & mask, x.b1 & mask, aab);
+    f32x16 aab = mfma32(f.a0, x.b0 & mask, zero);
+    aab = mfma32(f.a1, x.b1 & mask, aab);
     bound = max16(aab);
     if (G == 32) bound = max_halves(bound);
   }
@@ -584,6 +596,7 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
     }
   }
   const float bscale = (FMT == kMXFP4) ? panel_tmax(f) * 0x1p-17f : 0x1p-17f;
+  if (FMT != kMXFP4) with_abs(f);  // |T| once per run, for the per-output bound
   u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
   asm volatile("" : "+v"(ones));  // materialized once, kept in VGPRs
   float g = 0.0f;
@@ -705,10 +718,15 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
   if (a.n_exact && n_exact && lane == 0) atomicAdd(a.n_exact, n_exact);
 }
 
-// MXFP4 asks for 8 waves per SIMD (64 VGPRs): with 35 KB of LDS per
-// two-tile workgroup, four workgroups then share a CU.
+// 8 waves per SIMD (at most 64 VGPRs): with 35 KB of LDS per two-tile
+// workgroup, four workgroups then share a CU.  Without the bound NVFP4 and
+// INT4 took 68-70 VGPRs, which left room for three; four measured 6.6%
+// faster on the 16384x4096 NVFP4 workload.  At this bound the NVFP4 edge
+// path (quant_run<.., false>) keeps one register in scratch; the full-tile
+// path spills nothing.  Four-tile runs fit two workgroups per CU by their
+// LDS alone, so they ask for 4 waves per SIMD.
 template <int FMT, int TPW>
-__global__ __launch_bounds__(kQWaves * 64, (FMT == kMXFP4) ? 8 : 1) void quant_kernel(QuantArgs a) {
+__global__ __launch_bounds__(kQWaves * 64, TPW == 4 ? 4 : 8) void quant_kernel(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) QuantLds<TPW> L;
   int cg, tg;
   wg_coords(a.n_pg, a.n_tg, cg, tg);
