@@ -8,7 +8,8 @@ Bar:
     scale spread, bounded K) must match bit for bit, in fp32 and, after
     round-to-nearest-even, in bf16.  This pins nibble order, operand
     orientation, scale placement and the ragged edges, for both tile
-    sizes (64 x 64 for grids that would leave CUs idle, else 128 x 128).
+    sizes (64 x 64 for grids that would leave CUs idle, else 128 x 128)
+    and K from one 256-element step to several turns of the LDS ring.
   * General cases.  Each product of two E2M1 values and two E8M0 scales is
     exact in fp32, so any fp32 summation order of the K products errs by at
     most (K - 1) * 2^-24 * sum_k |a_k b_k|.  That is the tolerance, with
@@ -77,6 +78,9 @@ _EXACT = [
     (5, 300, 256, 127, 127),
     (1000, 3000, 256, 126, 128),  # 8 x 24 tiles of 128: the 128 x 128 kernel, ragged on both edges
     (1024, 3072, 512, 127, 127),  # the 128 x 128 kernel, whole tiles
+    (1000, 3000, 2304, 127, 127),  # 128 x 128, 9 steps of 256: the ring wraps mid-way
+    (77, 390, 4352, 127, 127),     # 64 x 64, 17 steps
+    (64, 64, 2048, 126, 128),      # 64 x 64, 8 steps: one full turn of its ring
 ]
 
 
