@@ -220,6 +220,8 @@ __device__ __forceinline__ u32x4 load16_nt(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+typedef const __attribute__((address_space(3))) uint8_t lds_cu8;
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -227,10 +229,17 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // write them into the accumulator of lanes (n, 0) and (n, 1).  Lane (i, h)
 // owns output row permuted_row(i): its T fragment (the MFMA A operand) is
 // exactly its half-row of T, and it forms the half-h partial sum; lane
-// l ^ 32 holds the other half.  The fragment is copied through an empty asm
+// l ^ 32 holds the other half.  Token n's channels of the panel come from
+// the lanes that hold them (readlane), or, with XLDS, from the staged tile
+// (LDS address `xtok`, its row at this panel; the same 16 bytes for every
+// lane of a half, a broadcast read).  XLDS costs 8 VGPRs in this path and
+// saves about 40 instructions per call; it is used where the register
+// budget allows it.  The fragment is copied through an empty asm
 // statement, so the compiler cannot hoist this rare path's float64
 // conversions of T out of the hot loop into registers that stay live.
-__device__ __forceinline__ void exact_panel(int n, const Frag& f, const XTile& x, f32x16& acc, float* lds, int lane) {
+template <bool XLDS>
+__device__ __forceinline__ void exact_panel(uint32_t xtok, const XTile& x, const Frag& f, f32x16& acc, float* lds,
+                                            int n, int lane) {
   // Addresses below derive from an opaque copy of the lane id, so the
   // compiler keeps their arithmetic inside this rarely taken path.
   int lds_off = 0;
@@ -240,15 +249,25 @@ __device__ __forceinline__ void exact_panel(int n, const Frag& f, const XTile& x
   const int row = permuted_row(i);
   u32x4 tk[2] = {f.t0, f.t1};
   asm volatile("" : "+v"(tk[0]), "+v"(tk[1]));
-  const u32x4 bk[2] = {x.b0, x.b1};
+  u32x4 bk[2] = {x.b0, x.b1};
+  if (XLDS) {
+    lds_cu8* xp = (lds_cu8*)(uintptr_t)(xtok + 16 * h);
+    bk[0] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(xp);
+    bk[1] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(xp + 32);
+  }
   double s = 0.0;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t x0 = __builtin_amdgcn_readlane(bk[kk][w], n);
-      uint32_t x1 = __builtin_amdgcn_readlane(bk[kk][w], n + 32);
-      uint32_t xw = h ? x1 : x0;
+      uint32_t xw;
+      if (XLDS) {
+        xw = bk[kk][w];
+      } else {
+        uint32_t x0 = __builtin_amdgcn_readlane(bk[kk][w], n);
+        uint32_t x1 = __builtin_amdgcn_readlane(bk[kk][w], n + 32);
+        xw = h ? x1 : x0;
+      }
       uint32_t tw = tk[kk][w];
       s = __builtin_fma((double)bf16_lo(tw), (double)bf16_lo(xw), s);
       s = __builtin_fma((double)bf16_hi(tw), (double)bf16_hi(xw), s);
@@ -350,9 +369,10 @@ __device__ __forceinline__ void wg_coords(int n_pg, int n_tg, int& pg, int& tg) 
 // group.  Output: this lane's 16 codes (two words) and its scale bits.
 // Groups whose scale decision falls within the accumulation error bound of
 // a boundary are recomputed exactly first.
-template <int FMT>
+template <int FMT, bool XLDS>
 __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float bound_scale, const Frag& f,
-                                                const XTile& x, float g, float* lds, int lane,
+                                                const XTile& x, uint32_t tile, int tile_stride, float g, float* lds,
+                                                int lane,
                                                 uint32_t& scale_bits, uint32_t& n_exact) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   float amax = max_abs16(acc);
@@ -373,7 +393,7 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
   if (pending) {
     while (pending) {
       int ln = __builtin_ctzll(pending) & 31;
-      exact_panel(ln, f, x, acc, lds, lane);
+      exact_panel<XLDS>(tile + ln * tile_stride, x, f, acc, lds, ln, lane);
       pending &= ~((1ull << ln) | (1ull << (ln + 32)));
       ++n_exact;  // wave-uniform count
     }
@@ -496,7 +516,7 @@ struct QuantLds {
 // L1 norms (of a token pair, see below); bscale is max|T| * 2^-17.  INT4 and NVFP4 scales have much denser
 // boundaries, so they use the per-output bound max_k sum_j |T_kj x_j| from
 // an |T| x |x| MFMA, with bscale = 2^-17.
-template <int FMT>
+template <int FMT, bool XLDS>
 __device__ __forceinline__ void panel_step(uint8_t* row, float* ybuf, const Frag& f, const u32x4& ones, float bscale,
                                            float g, int wave, int lane, uint32_t& n_exact) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
@@ -530,7 +550,10 @@ __device__ __forceinline__ void panel_step(uint8_t* row, float* ybuf, const Frag
     if (G == 32) bound = max_halves(bound);
   }
   uint32_t sbits;
-  const u32x2 w = quantize_panel<FMT>(acc, bound, bscale, f, x, g, ybuf, lane, sbits, n_exact);
+  // LDS address of row 0 of the staged tile at this wave's panel: the exact
+  // recompute reads a token's channels there.
+  const uint32_t tile = (uint32_t)(uintptr_t)(lds_cu8*)(row - (lane & 31) * kXRow + wave * 64);
+  const u32x2 w = quantize_panel<FMT, XLDS>(acc, bound, bscale, f, x, tile, kXRow, g, ybuf, lane, sbits, n_exact);
   // Every lane of the wave has read its operands before any lane writes:
   // the reads above feed the MFMAs whose results the writes depend on.
   *reinterpret_cast<u32x2*>(row + wave * 64 + 8 * h) = w;
@@ -652,7 +675,12 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       if (!FULL && u >= n_tiles) break;
-      panel_step<FMT>(row + u * (32 * kXRow), L.y[wave], f, ones, bscale, g, wave, lane, n_exact);
+      // The staged-tile read in the exact path needs registers that only
+      // the four-tile INT4 kernel has to spare (its LDS allows two
+      // workgroups per CU, so it is not held to 64 VGPRs); INT4 takes that
+      // path often (see quantize_panel).
+      panel_step<FMT, FMT == kINT4 && TPW == 4>(row + u * (32 * kXRow), L.y[wave], f, ones, bscale, g, wave, lane,
+                                                 n_exact);
     }
   }
   __syncthreads();
