@@ -125,6 +125,24 @@ def test_qwen3_8b_layer_shapes_sampled(layer):
     _check_tol(got[np.ix_(rows, cols)], ref, absref, K, False)
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 64, 2048), (64, 64, 4096), (2048, 2048, 2048), (1024, 4096, 4096)])
+def test_fresh_operands_every_call(M, N, K):
+    """Several calls in a row, each with new A operands.  A load that has not
+    landed when its stage is read would leave the previous call's data in
+    LDS; with identical inputs on every call that stale data would be right
+    and hide the error, so every call here gets different codes and
+    scales."""
+    bc, bsc = gen_mx_operand(N, K, seed=12, scale_lo=124, scale_hi=130)
+    rows = np.unique(np.r_[np.arange(0, M, max(1, M // 48)), M - 1])
+    cols = np.unique(np.r_[np.arange(0, N, max(1, N // 48)), N - 1])
+    for call in range(5):
+        ac, asc = gen_mx_operand(M, K, seed=300 + call, scale_lo=124, scale_hi=130)
+        got = _gemm(ac, asc, bc, bsc, torch.float32)
+        ref = gemm.gemm_mxfp4_ref(ac[rows], asc[rows], bc[cols], bsc[cols])
+        absref = gemm.gemm_mxfp4_abs_ref(ac[rows], asc[rows], bc[cols], bsc[cols])
+        _check_tol(got[np.ix_(rows, cols)], ref, absref, K, False)
+
+
 def test_zero_rows_is_a_no_op():
     from mxfp4_activation_amd import ops
 
