@@ -34,6 +34,7 @@ struct QuantArgs {
   int n_panels;            // ceil(K / 32)
   int n_pg;                // ceil(n_panels / kPanelsPerTile): tiles along K
   int n_tg;                // ceil(n_tiles / tiles_per_wave)
+  int token_major;         // workgroup order: nonzero = token-major, 0 = panel-major
 };
 
 struct TransformArgs {

@@ -352,15 +352,27 @@ __device__ __forceinline__ float err_bound(float bound, float bound_scale, float
 
 // Workgroup -> (panel group, token group).  Workgroups are dispatched
 // round-robin over the 8 XCDs.  When the count divides evenly, each XCD
-// gets a contiguous range in panel-major order, so its L2 fetches each T
-// panel once.
-__device__ __forceinline__ void wg_coords(int n_pg, int n_tg, int& pg, int& tg) {
+// gets a contiguous range of the logical order:
+// - panel-major (token_major == 0): an XCD covers a few panels over all
+//   tokens, so its L2 fetches each T panel once.  When the whole grid is
+//   resident at once, every T fetch competes with the first X loads, and
+//   this order keeps them to 1/8 of T per XCD.
+// - token-major (token_major != 0): an XCD covers whole token rows, so the
+//   workgroups resident together read contiguous rows and complete each
+//   row's scale line in one L2.  With several waves of workgroups the T
+//   fetches are spread over the waves.
+__device__ __forceinline__ void wg_coords(int n_pg, int n_tg, int token_major, int& pg, int& tg) {
   int b = blockIdx.x;
   int n = n_pg * n_tg;
   int logical = b;
   if ((n & 7) == 0) logical = (b & 7) * (n >> 3) + (b >> 3);
-  pg = logical / n_tg;
-  tg = logical - pg * n_tg;
+  if (token_major) {
+    tg = logical / n_pg;
+    pg = logical - tg * n_pg;
+  } else {
+    pg = logical / n_tg;
+    tg = logical - pg * n_tg;
+  }
 }
 
 // Per-group scale and code computation for one panel of one 32-token tile.
@@ -757,7 +769,7 @@ template <int FMT, int TPW>
 __global__ __launch_bounds__(kQWaves * 64, TPW == 4 ? 4 : 8) void quant_kernel(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) QuantLds<TPW> L;
   int cg, tg;
-  wg_coords(a.n_pg, a.n_tg, cg, tg);
+  wg_coords(a.n_pg, a.n_tg, a.token_major, cg, tg);
   const bool full = ((int64_t)(tg + 1) * TPW * 32 <= a.M) && (a.K % (kPanels * 32) == 0) && a.K <= (1 << 26);
   if (full) quant_run<FMT, TPW, true>(a, L, cg, tg);
   else quant_run<FMT, TPW, false>(a, L, cg, tg);
@@ -770,7 +782,7 @@ template <int FMT, int TPW>
 __global__ __launch_bounds__(kQWaves * 64) void absmax_kernel(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) QuantLds<TPW> L;
   int cg, tg;
-  wg_coords(a.n_pg, a.n_tg, cg, tg);
+  wg_coords(a.n_pg, a.n_tg, a.token_major, cg, tg);
   const bool full = ((int64_t)(tg + 1) * TPW * 32 <= a.M) && (a.K % (kPanels * 32) == 0) && a.K <= (1 << 26);
   if (full) quant_run<FMT, TPW, true, true>(a, L, cg, tg);
   else quant_run<FMT, TPW, false, true>(a, L, cg, tg);
@@ -783,7 +795,7 @@ __global__ __launch_bounds__(kWaves * 64) void transform_kernel(TransformArgs a)
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   int pg, tg;
-  wg_coords(a.n_pg, a.n_tg, pg, tg);
+  wg_coords(a.n_pg, a.n_tg, 0, pg, tg);
   const int p = pg * kWaves + wave;
   if (p >= a.n_panels) return;
   const int n = lane & 31, h = lane >> 5;
