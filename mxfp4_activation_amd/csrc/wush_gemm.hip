@@ -286,57 +286,77 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   }
   wait_barrier<0>();
 
-  // Add the two groups' partial tiles.  TM = 2: group g finishes MFMA tile
-  // row i == g and hands tile row 1 - g to its partner wave.  TM = 1: group
-  // g finishes accumulator registers 8 g .. 8 g + 7 and hands the others.
+  // Add the two groups' partial tiles through LDS, then write the summed
+  // tile to LDS as fp32 (rows padded): lane (j + 32h) of an MFMA tile holds
+  // rows 8 (r / 4) + 4 h + r % 4 of column j in accumulator register r.
   f32x4* xch = reinterpret_cast<f32x4*>(L);
-  constexpr int kKeep = TM == 2 ? 2 : 1;   // tiles kept per wave (x 16 or 8 registers)
-  constexpr int kRegs = TM == 2 ? 16 : 8;  // registers kept per tile
-  f32x16 give[kKeep], fin[kKeep];
+  float* ct = reinterpret_cast<float*>(L);
+  const int partner = wave ^ 4;
+  if constexpr (TM == 2) {
+    // Group g finishes MFMA tile row g and hands tile row 1 - g to its
+    // partner wave.
+    f32x16 give[2], fin[2];
 #pragma unroll
-  for (int jt = 0; jt < kKeep; ++jt) {  // constant indices keep acc in registers
-    if constexpr (TM == 2) {
+    for (int jt = 0; jt < 2; ++jt) {  // constant indices keep acc in registers
       give[jt] = grp ? acc[0][jt] : acc[1][jt];
       fin[jt] = grp ? acc[1][jt] : acc[0][jt];
-    } else {
-      fin[jt] = acc[0][0];
-      give[jt] = acc[0][0];
     }
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = give[jt][4 * q + e];
+        xch[((wave * 2 + jt) * 4 + q) * 64 + lane] = v;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = xch[((partner * 2 + jt) * 4 + q) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fin[jt][4 * q + e] += v[e];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 64 * wm + 32 * grp + 8 * (r / 4) + 4 * lh + (r % 4);
+        ct[row * Gm::kCRow + 64 * wn + 32 * jt + li] = fin[jt][r];
+      }
+  } else {
+    // Group g finishes accumulator registers 8 g .. 8 g + 7 and hands the
+    // other eight to its partner.  The halves are picked once, by whole
+    // vectors, so that every register index below is a constant: an index
+    // that depends on the group compiles to a select over all 16 registers
+    // for every element moved (about 1300 instructions, ~4 us per launch).
+    f32x4 keep[2], hand[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = acc[0][0][4 * q + e], hi = acc[0][0][8 + 4 * q + e];
+        keep[q][e] = grp ? hi : lo;
+        hand[q][e] = grp ? lo : hi;
+      }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) xch[(wave * 2 + q) * 64 + lane] = hand[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) keep[q] += xch[(partner * 2 + q) * 64 + lane];
+    __syncthreads();
+    // keep[q][e] is register r = 8 g + 4 q + e: row 16 g + 8 q + 4 h + e.
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 32 * wm + 16 * grp + 8 * q + 4 * lh + e;
+        ct[row * Gm::kCRow + 32 * wn + li] = keep[q][e];
+      }
   }
-  const int partner = wave ^ 4;
-  const int give_base = TM == 2 ? 0 : (grp ? 0 : 8);  // TM = 1: the registers this group hands over
-  const int keep_base = TM == 2 ? 0 : (grp ? 8 : 0);
-#pragma unroll
-  for (int jt = 0; jt < kKeep; ++jt)
-#pragma unroll
-    for (int q = 0; q < kRegs / 4; ++q) {
-      f32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = give[jt][give_base + 4 * q + e];
-      xch[((wave * kKeep + jt) * (kRegs / 4) + q) * 64 + lane] = v;
-    }
-  __syncthreads();
-#pragma unroll
-  for (int jt = 0; jt < kKeep; ++jt)
-#pragma unroll
-    for (int q = 0; q < kRegs / 4; ++q) {
-      const f32x4 v = xch[((partner * kKeep + jt) * (kRegs / 4) + q) * 64 + lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) fin[jt][keep_base + 4 * q + e] += v[e];
-    }
-  __syncthreads();
-
-  // Output tile to LDS (fp32, rows padded): lane (j + 32h) of an MFMA tile
-  // holds rows 8 (r / 4) + 4 h + r % 4 of column j.
-  float* ct = reinterpret_cast<float*>(L);
-#pragma unroll
-  for (int jt = 0; jt < kKeep; ++jt)
-#pragma unroll
-    for (int rr = 0; rr < kRegs; ++rr) {
-      const int r = keep_base + rr;
-      const int row = (TM == 2 ? 64 * wm + 32 * grp : 32 * wm) + 8 * (r / 4) + 4 * lh + (r % 4);
-      ct[row * Gm::kCRow + 32 * TM * wn + 32 * jt + li] = fin[jt][r];
-    }
   __syncthreads();
 
   // Row-contiguous stores: each thread writes 4 (fp32) or 8 (bf16) columns
