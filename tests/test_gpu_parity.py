@@ -217,8 +217,12 @@ def test_full_size_sampled_rows(name):
 # ragged last run: M = 4100 at K = 4096 (two-tile runs, the last run one
 # partial tile) and M = 4136 at K = 8192 (four-tile runs, the last run two
 # tiles, the second partial).  The oracle checks sampled rows, which
-# include every row of the last two tiles.
-@pytest.mark.parametrize("fmt,M,K", [("mxfp4", 4100, 4096), ("int4", 4136, 8192), ("nvfp4", 4100, 4096)])
+# include every row of the last two tiles.  All of these grids exceed one
+# resident wave of workgroups, so they take the token-major order.
+# M = 4600 at K = 4128 adds a partial 256-channel column: 17 x 72 = 1224
+# workgroups, a multiple of 8, so the XCD remap applies as well.
+@pytest.mark.parametrize("fmt,M,K", [("mxfp4", 4100, 4096), ("int4", 4136, 8192), ("nvfp4", 4100, 4096),
+                                     ("mxfp4", 4600, 4128), ("nvfp4", 4600, 4128)])
 def test_long_runs_with_ragged_tail(fmt, M, K):
     print("case", fmt, M, K, flush=True)
     G = 16 if fmt == "nvfp4" else 32
