@@ -91,6 +91,10 @@ def parse():
     ap.add_argument("--gemm-layers", action="store_true",
                     help="per-layer Eq. 10 forward (transform + quantize + MXFP4 GEMM) against the bf16 GEMM "
                          "on Qwen3-8B layer shapes at 1024 tokens, instead of the headline measurement")
+    ap.add_argument("--gemm-fused", action="store_true",
+                    help="with --gemm-layers: measure the fused projections instead (q|k|v as one 6144 x 4096 "
+                         "layer, gate|up as one 24576 x 4096 layer, each with one transform bank built from the "
+                         "concatenated weight)")
     ap.add_argument("--layer-loss", action="store_true",
                     help="layerwise loss (Eq. 5) of I / H / WUS / WUSH in MXFP4, NVFP4 and INT4 on synthetic "
                          "Qwen3-8B-shaped layers, computed by the kernels, instead of the headline measurement")
@@ -368,14 +372,14 @@ def gemm_layers(args) -> None:
     import torch
 
     from mxfp4_activation_amd import ops, transforms
-    from synthetic.gemm_operands import GEMM_TOKENS, QWEN3_8B_LAYERS
+    from synthetic.gemm_operands import GEMM_TOKENS, QWEN3_8B_FUSED, QWEN3_8B_LAYERS
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     M, G = GEMM_TOKENS, 32
     gen = torch.Generator(device="cpu").manual_seed(2024)
     shapes = {}
-    for name, nk in QWEN3_8B_LAYERS.items():
+    for name, nk in (QWEN3_8B_FUSED if args.gemm_fused else QWEN3_8B_LAYERS).items():
         shapes.setdefault(nk, []).append(name)
     rows = []
     for (N, K), names in shapes.items():
@@ -448,7 +452,8 @@ def gemm_layers(args) -> None:
                "bf16_gemm_tflops": round(flop / us["bf16"] / 1e6, 1)}
         rows.append(row)
         print(json.dumps(row), flush=True)
-    print(json.dumps({"comparison": "Eq. 10 forward per Qwen3-8B layer shape, 1024 tokens, bf16 output, hot caches",
+    what = "fused Qwen3-8B projections" if args.gemm_fused else "Qwen3-8B layer shape"
+    print(json.dumps({"comparison": "Eq. 10 forward per %s, 1024 tokens, bf16 output, hot caches" % what,
                       "variants": {"bf16": "torch.matmul (hipBLASLt)",
                                    "wush_quant_fp4": "wush_quant_mxfp4 (T_wush) + wush_gemm_mxfp4",
                                    "h_quant_fp4": "same kernels with the blockwise Hadamard bank",

@@ -23,6 +23,14 @@ QWEN3_8B_LAYERS: Dict[str, Tuple[int, int]] = {
     "down_proj": (4096, 12288),
 }
 
+# Projections that share their input, run as one linear layer with the
+# concatenated weight (one transform bank built from that weight): q|k|v and
+# gate|up.
+QWEN3_8B_FUSED: Dict[str, Tuple[int, int]] = {
+    "qkv_proj": (4096 + 1024 + 1024, 4096),
+    "gate_up_proj": (2 * 12288, 4096),
+}
+
 # Token batch of the per-layer GEMM measurement.
 GEMM_TOKENS = 1024
 
