@@ -95,6 +95,8 @@ def parse():
                     help="with --gemm-layers: measure the fused projections instead (q|k|v as one 6144 x 4096 "
                          "layer, gate|up as one 24576 x 4096 layer, each with one transform bank built from the "
                          "concatenated weight)")
+    ap.add_argument("--gemm-tokens", type=int, default=0,
+                    help="with --gemm-layers: token batch M (default 1024)")
     ap.add_argument("--layer-loss", action="store_true",
                     help="layerwise loss (Eq. 5) of I / H / WUS / WUSH in MXFP4, NVFP4 and INT4 on synthetic "
                          "Qwen3-8B-shaped layers, computed by the kernels, instead of the headline measurement")
@@ -376,7 +378,9 @@ def gemm_layers(args) -> None:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    M, G = GEMM_TOKENS, 32
+    M, G = (args.gemm_tokens or GEMM_TOKENS), 32
+    if M < 1:
+        raise SystemExit("--gemm-tokens must be positive")
     gen = torch.Generator(device="cpu").manual_seed(2024)
     shapes = {}
     for name, nk in (QWEN3_8B_FUSED if args.gemm_fused else QWEN3_8B_LAYERS).items():
@@ -453,7 +457,7 @@ def gemm_layers(args) -> None:
         rows.append(row)
         print(json.dumps(row), flush=True)
     what = "fused Qwen3-8B projections" if args.gemm_fused else "Qwen3-8B layer shape"
-    print(json.dumps({"comparison": "Eq. 10 forward per %s, 1024 tokens, bf16 output, hot caches" % what,
+    print(json.dumps({"comparison": "Eq. 10 forward per %s, %d tokens, bf16 output, hot caches" % (what, M),
                       "variants": {"bf16": "torch.matmul (hipBLASLt)",
                                    "wush_quant_fp4": "wush_quant_mxfp4 (T_wush) + wush_gemm_mxfp4",
                                    "h_quant_fp4": "same kernels with the blockwise Hadamard bank",
