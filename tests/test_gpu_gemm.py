@@ -108,12 +108,13 @@ def test_wide_scale_range_within_fp32_bound(M, N, K, out):
     print(f"max err / bound = {ratio:.3g}")
 
 
-@pytest.mark.parametrize("layer", ["q_proj", "k_proj", "gate_proj", "down_proj"])
-def test_qwen3_8b_layer_shapes_sampled(layer):
-    """Full-size operands (1024 tokens); a grid of sampled rows and columns,
+@pytest.mark.parametrize("layer,M", [("q_proj", GEMM_TOKENS), ("k_proj", GEMM_TOKENS), ("gate_proj", GEMM_TOKENS),
+                                     ("down_proj", GEMM_TOKENS), ("q_proj", 8192), ("k_proj", 8192)])
+def test_qwen3_8b_layer_shapes_sampled(layer, M):
+    """Full-size operands (1024 tokens, and 8192, whose grids run several
+    waves of 128 x 128 workgroups); a grid of sampled rows and columns,
     including the first and last ones of every edge tile, is checked."""
     N, K = QWEN3_8B_LAYERS[layer]
-    M = GEMM_TOKENS
     ac, asc = gen_mx_operand(M, K, seed=31, scale_lo=112, scale_hi=124)
     bc, bsc = gen_mx_operand(N, K, seed=32, scale_lo=116, scale_hi=122)
     got = _gemm(ac, asc, bc, bsc, torch.float32)
