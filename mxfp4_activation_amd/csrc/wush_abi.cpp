@@ -91,15 +91,20 @@ void plan(int64_t M, int64_t K, int64_t* n_tiles, int64_t* tpw, int* n_panels, i
 // Quant kernel split: a workgroup (8 waves) owns a 256-channel column of
 // the input and a run of TPW 32-token tiles, all loaded at entry.  TPW is
 // the longest run up to a per-format cap that still gives at least 1024
-// workgroups (four per CU), so that several workgroups share each CU and
-// cover each other's waits.  The cap is 2 for MXFP4 and NVFP4: longer runs
-// need twice the LDS per workgroup (two per CU instead of four), which
-// measured slower on every large batch.  INT4 does twice the vector work per
-// tile and is compute-bound; for it 4 tiles measured faster than 2.
-// WUSH_TILES_PER_WG overrides the choice for tuning.
+// workgroups, so that several workgroups share each CU and cover each
+// other's waits.  Two-tile runs fit four workgroups per CU, three-tile runs
+// three.  The caps, measured:
+// - MXFP4: 3.  On 8192 x 14336, three-tile runs measured 2.6% faster than
+//   two.  4096 x 4096 keeps two-tile runs, since three would leave fewer
+//   than 1024 workgroups; forced, they measured 10% slower there.
+// - NVFP4: 2.  Three-tile runs measured 1-2% slower on 16384 x 4096.
+// - INT4: 3.  It does twice the vector work per tile and is compute-bound;
+//   three-tile runs (with the exact recompute reading LDS) measured 10%
+//   faster than four-tile runs, and four faster than two.
+// WUSH_TILES_PER_WG (1, 2 or 3) overrides the choice for tuning.
 //
 // The workgroup order is panel-major while the whole grid fits on the chip
-// at once (256 CUs x 4 workgroups, or x 2 for four-tile runs), and
+// at once (256 CUs x 4 workgroups, or x 3 for three-tile runs), and
 // token-major beyond that.  On 8192 x 14336 MXFP4 (seven waves of
 // workgroups) token-major measured 2.4% faster; on 4096 x 4096 (one wave)
 // it measured 1% slower; on the NVFP4 and INT4 batches the two tie.
@@ -107,17 +112,17 @@ void plan_quant(int fmt, int64_t M, int64_t K, wush::QuantArgs& a) {
   a.n_tiles = (M + 31) / 32;
   a.n_panels = (int)((K + 31) / 32);
   a.n_pg = (a.n_panels + wush::kPanelsPerTile - 1) / wush::kPanelsPerTile;
-  const int64_t target_wg = 8192 / wush::kPanelsPerTile;  // 4 eight-wave workgroups per CU
-  int64_t t = fmt == wush::kINT4 ? 4 : 2;
-  while (t > 1 && (int64_t)a.n_pg * ((a.n_tiles + t - 1) / t) < target_wg) t >>= 1;
+  const int64_t target_wg = 8192 / wush::kPanelsPerTile;  // 1024 eight-wave workgroups
+  int64_t t = fmt == wush::kNVFP4 ? 2 : 3;
+  while (t > 1 && (int64_t)a.n_pg * ((a.n_tiles + t - 1) / t) < target_wg) --t;
   static const int64_t env = [] {
     const char* s = getenv("WUSH_TILES_PER_WG");
     return s ? (int64_t)atoll(s) : (int64_t)0;
   }();
-  if (env == 1 || env == 2 || env == 4) t = env;
+  if (env >= 1 && env <= 3) t = env;
   a.tiles_per_wave = t;
   a.n_tg = (int)((a.n_tiles + t - 1) / t);
-  const int64_t resident = 256 * (t == 4 ? 2 : 4);
+  const int64_t resident = 256 * (t == 3 ? 3 : 4);
   a.token_major = (int64_t)a.n_pg * a.n_tg > resident ? 1 : 0;
 }
 

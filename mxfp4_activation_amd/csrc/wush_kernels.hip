@@ -688,10 +688,10 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
     for (int u = 0; u < TPW; ++u) {
       if (!FULL && u >= n_tiles) break;
       // The staged-tile read in the exact path needs registers that only
-      // the four-tile INT4 kernel has to spare (its LDS allows two
-      // workgroups per CU, so it is not held to 64 VGPRs); INT4 takes that
-      // path often (see quantize_panel).
-      panel_step<FMT, FMT == kINT4 && TPW == 4>(row + u * (32 * kXRow), L.y[wave], f, ones, bscale, g, wave, lane,
+      // the three-tile kernels have to spare (their LDS allows three
+      // workgroups per CU, so they are held to 85 VGPRs, not 64); INT4
+      // takes that path often (see quantize_panel).
+      panel_step<FMT, FMT == kINT4 && TPW == 3>(row + u * (32 * kXRow), L.y[wave], f, ones, bscale, g, wave, lane,
                                                  n_exact);
     }
   }
@@ -763,10 +763,10 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
 // INT4 took 68-70 VGPRs, which left room for three; four measured 6.6%
 // faster on the 16384x4096 NVFP4 workload.  At this bound the NVFP4 edge
 // path (quant_run<.., false>) keeps one register in scratch; the full-tile
-// path spills nothing.  Four-tile runs fit two workgroups per CU by their
-// LDS alone, so they ask for 4 waves per SIMD.
+// path spills nothing.  Three-tile runs (51 KB) fit three workgroups per CU
+// by their LDS alone, so they ask for 6 waves per SIMD.
 template <int FMT, int TPW>
-__global__ __launch_bounds__(kQWaves * 64, TPW == 4 ? 4 : 8) void quant_kernel(QuantArgs a) {
+__global__ __launch_bounds__(kQWaves * 64, TPW == 3 ? 6 : 8) void quant_kernel(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) QuantLds<TPW> L;
   int cg, tg;
   wg_coords(a.n_pg, a.n_tg, a.token_major, cg, tg);
@@ -858,7 +858,7 @@ static hipError_t launch_quant_fmt(const QuantArgs& a, int n_wg, hipStream_t s) 
   switch (a.tiles_per_wave) {
     case 1: hipLaunchKernelGGL((quant_kernel<FMT, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((quant_kernel<FMT, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((quant_kernel<FMT, 4>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((quant_kernel<FMT, 3>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -886,12 +886,12 @@ static void launch_absmax_fmt(const QuantArgs& a, int n_wg, hipStream_t s) {
   switch (a.tiles_per_wave) {
     case 1: hipLaunchKernelGGL((absmax_kernel<FMT, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((absmax_kernel<FMT, 2>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((absmax_kernel<FMT, 4>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((absmax_kernel<FMT, 3>), grid, block, 0, s, a); break;
   }
 }
 
 hipError_t launch_absmax(int G, const QuantArgs& a, int n_wg, hipStream_t s) {
-  if (a.tiles_per_wave != 1 && a.tiles_per_wave != 2 && a.tiles_per_wave != 4) return hipErrorInvalidValue;
+  if (a.tiles_per_wave < 1 || a.tiles_per_wave > 3) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(1), 0, s, a.amax_bits, 0u);
   if (n_wg == 0) return hipGetLastError();
   if (G == 32) launch_absmax_fmt<kMXFP4>(a, n_wg, s);

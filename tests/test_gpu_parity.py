@@ -213,16 +213,24 @@ def test_full_size_sampled_rows(name):
     print(name, rep, "exact groups:", n, "of", wl.M * wl.C, flush=True)
 
 
-# Batches big enough that workgroups take runs of 2 or 4 tiles, with a
-# ragged last run: M = 4100 at K = 4096 (two-tile runs, the last run one
-# partial tile) and M = 4136 at K = 8192 (four-tile runs, the last run two
-# tiles, the second partial).  The oracle checks sampled rows, which
-# include every row of the last two tiles.  All of these grids exceed one
-# resident wave of workgroups, so they take the token-major order.
-# M = 4600 at K = 4128 adds a partial 256-channel column: 17 x 72 = 1224
-# workgroups, a multiple of 8, so the XCD remap applies as well.
+# Batches big enough that workgroups take runs of 2 or 3 tiles, with a
+# ragged last run:
+# - MXFP4 and NVFP4, M = 4100 at K = 4096: two-tile runs, the last run one
+#   partial tile;
+# - INT4, M = 4136 at K = 8192: three-tile runs, the last run one partial
+#   tile; M = 4168: the last run two tiles, the second partial;
+# - MXFP4, M = 8200 at K = 4096: three-tile runs, the last run two tiles,
+#   the second partial;
+# - M = 4600 at K = 4128 and M = 8200 at K = 4128 add a partial 256-channel
+#   column (17 panel groups): 17 x 72 = 1224 two-tile workgroups, a multiple
+#   of 8, so the XCD remap applies; 17 x 86 = 1462 three-tile ones, which is
+#   not.
+# All of these grids exceed one resident wave of workgroups, so they take
+# the token-major order.  The oracle checks sampled rows, which include
+# every row of the last two tiles.
 @pytest.mark.parametrize("fmt,M,K", [("mxfp4", 4100, 4096), ("int4", 4136, 8192), ("nvfp4", 4100, 4096),
-                                     ("mxfp4", 4600, 4128), ("nvfp4", 4600, 4128)])
+                                     ("int4", 4168, 8192), ("mxfp4", 8200, 4096),
+                                     ("mxfp4", 4600, 4128), ("nvfp4", 4600, 4128), ("mxfp4", 8200, 4128)])
 def test_long_runs_with_ragged_tail(fmt, M, K):
     print("case", fmt, M, K, flush=True)
     G = 16 if fmt == "nvfp4" else 32
