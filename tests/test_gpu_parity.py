@@ -306,6 +306,26 @@ def test_absmax_and_global_scale(G, rows, blocks):
         assert g == float(np.float32(np.float32(amax) / np.float32(2688.0)))
 
 
+@pytest.mark.parametrize("planted", [8199, 4111])
+def test_absmax_three_tile_runs(planted):
+    """G = 32 AbsMax on 8200 x 4096, which takes three-tile runs with a
+    ragged last run (two tiles, the second partial).  One row is scaled by
+    1000 so that it holds the tensor's maximum; the oracle computes that row
+    alone.  Row 8199 sits in the last partial tile, row 4111 mid-tensor."""
+    from mxfp4_activation_amd import ops
+
+    _, tb = cases.transforms("llama8b_mxfp4")
+    M, K = 8200, tb.shape[0] * 32
+    rng = np.random.default_rng(planted)
+    X = rng.standard_normal((M, K))  # light tails: no other row comes near the planted one
+    X[planted] *= 1000.0
+    xb = f64_to_bf16_bits(X)
+    y, A = quant.transform_ref(xb[planted:planted + 1], tb, return_abs=True)
+    ref = float(np.abs(y).max())
+    amax = float(ops.transformed_absmax(_dev_bf16(xb), _dev_bf16(tb)).item())
+    assert abs(amax - ref) <= (2.0 ** -17) * A.max() + (2.0 ** -21) * ref, (amax, ref)
+
+
 def test_absmax_empty_is_zero():
     from mxfp4_activation_amd import ops
 
