@@ -262,7 +262,10 @@ static wush_status absmax_common(const void* X, const void* T, int64_t M, int64_
   a.K = K;
   int64_t n_wg = 0;
   if (M > 0) {
-    plan_quant(G == 16 ? wush::kNVFP4 : wush::kMXFP4, M, K, a);
+    // The pass does no quantization work, so it takes MXFP4's tile cap
+    // for both G: on 16384 x 4096 with G = 16, three-tile runs measured
+    // 34.3 against 40.5 us for the two-tile runs NVFP4 quantization uses.
+    plan_quant(wush::kMXFP4, M, K, a);
     n_wg = (int64_t)a.n_pg * a.n_tg;
     if (n_wg > 0x7FFFFFFF) return fail(WUSH_EINVAL, "problem too large for one launch");
   } else {
