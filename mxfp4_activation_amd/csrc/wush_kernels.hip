@@ -403,6 +403,22 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
   }
   uint64_t pending = __ballot(unsure);
   if (pending) {
+    // MXFP4: a token whose channels in this panel are all zero (either
+    // sign) has y = 0 exactly, and the matrix cores return exactly zero for
+    // it, so it needs no recompute.  Zero-padded rows would otherwise all
+    // land here: the bound's 2^-120 term leaves their interval across
+    // several E8M0 codes.  (The INT4 and NVFP4 decisions are already
+    // settled for them: fp16 and E4M3 both round that interval to 0.)
+    if (FMT == kMXFP4) {
+      typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+      const uint32_t xo = tile + (uint32_t)((lane & 31) * tile_stride + 16 * (lane >> 5));
+      const u32x4 q0 = *reinterpret_cast<lds_u32x4*>((lds_cu8*)(uintptr_t)xo);
+      const u32x4 q1 = *reinterpret_cast<lds_u32x4*>((lds_cu8*)(uintptr_t)(xo + 32));
+      const uint32_t any = (q0[0] | q0[1] | q0[2] | q0[3] | q1[0] | q1[1] | q1[2] | q1[3]) & 0x7FFF7FFFu;
+      const uint64_t zl = __ballot(any == 0u);
+      const uint64_t zt = zl & (zl >> 32) & 0xFFFFFFFFull;  // both halves of token n zero
+      pending &= ~(zt | (zt << 32));
+    }
     while (pending) {
       int ln = __builtin_ctzll(pending) & 31;
       exact_panel<XLDS>(tile + ln * tile_stride, x, f, acc, lds, ln, lane);
@@ -518,6 +534,7 @@ template <int TPW>
 struct QuantLds {
   uint8_t xs[TPW][32 * kXRow];  // activation tiles; codes and scales in place
   float y[kQWaves][32];         // exact-recompute exchange, per wave
+  uint32_t red[2][kQWaves];     // AbsMax pass: per-wave maxima of its two reductions
 };
 
 // Contract and quantize panel `wave` of one staged tile; write its codes and
@@ -575,6 +592,111 @@ __device__ __forceinline__ void panel_step(uint8_t* row, float* ybuf, const Frag
     if (h == 0) *reinterpret_cast<uint16_t*>(row + kScaleOff + 2 * wave) = (uint16_t)sbits;
   } else {
     row[kScaleOff + 2 * wave + h] = (uint8_t)sbits;
+  }
+}
+
+// Largest value of a non-negative float over the workgroup: wave maximum,
+// then one LDS slot per wave.  Every thread gets the result.  Non-negative
+// floats order like their bit patterns.
+__device__ __forceinline__ float block_max_nonneg(float v, uint32_t* slots, int wave, int lane) {
+  uint32_t b = __float_as_uint(v);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t w = (uint32_t)__shfl_xor((int)b, o, 64);
+    b = b > w ? b : w;
+  }
+  if (lane == 0) slots[wave] = b;
+  __syncthreads();
+  uint32_t r = slots[0];
+#pragma unroll
+  for (int i = 1; i < kQWaves; ++i) r = r > slots[i] ? r : slots[i];
+  return __uint_as_float(r);
+}
+
+// The exact max |y| over one run of staged tiles (the per-tensor AbsMax
+// behind NVFP4's global scale), folded into *a.amax_bits.
+//
+// Pass 1 bounds every output: with A_k = sum_j |T_kj x_j| (an |T| x |x|
+// MFMA), the fp32 matrix-core value differs from the exactly rounded y_k
+// by at most d_k = 2^-17 A_k + 2^-21 |y^_k| (+ 2^-120 for flushed
+// products), the bound the quantizer's scale guard uses.  Each lane keeps
+// a lower bound on the largest |y| it holds, amax - D with D the largest
+// d_k of the lane; the workgroup's largest lower bound `lo` is then a
+// lower bound on the run's exact maximum.
+// Pass 2 revisits only the tiles where some output's upper bound |y^_k| +
+// d_k reaches lo.  Those outputs are the only ones that can hold the
+// maximum; the tokens that own them are recomputed in float64 and rounded
+// once to fp32 (exact_panel), and the maximum over the recomputed values is
+// the run's exact maximum.  Outputs with A_k = 0 are exactly zero.
+template <int FMT, int TPW, bool FULL>
+__device__ __forceinline__ void amax_run(const QuantArgs& a, QuantLds<TPW>& L, Frag f, bool panel_ok, int n_tiles,
+                                         int wave, int lane) {
+  const u32x4 mask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
+  with_abs(f);
+  const int h = lane >> 5;
+  float lo = 0.0f;
+  float hi_t[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) hi_t[u] = -1.0f;
+  if (panel_ok) {
+    const uint8_t* row = L.xs[0] + (lane & 31) * kXRow + wave * 64 + 16 * h;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (!FULL && u >= n_tiles) break;
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(row + u * (32 * kXRow));
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(row + u * (32 * kXRow) + 32);
+      const f32x16 zero = {};
+      f32x16 acc = mfma32(f.t0, b0, zero);
+      acc = mfma32(f.t1, b1, acc);
+      f32x16 aab = mfma32(f.a0, b0 & mask, zero);
+      aab = mfma32(f.a1, b1 & mask, aab);
+      const float am = max_abs16(acc);
+      const float bnd = max16(aab);
+      const float d = err_bound(bnd, 0x1p-17f, am);
+      lo = fmaxf(lo, am - d);
+      hi_t[u] = am + d;
+    }
+  }
+  const float lo_wg = block_max_nonneg(lo, L.red[0], wave, lane);
+
+  float m = 0.0f;
+  if (panel_ok) {
+    const uint8_t* row = L.xs[0] + (lane & 31) * kXRow + wave * 64 + 16 * h;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (!FULL && u >= n_tiles) break;
+      if (!__ballot(hi_t[u] >= lo_wg)) continue;
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(row + u * (32 * kXRow));
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(row + u * (32 * kXRow) + 32);
+      const f32x16 zero = {};
+      f32x16 acc = mfma32(f.t0, b0, zero);
+      acc = mfma32(f.t1, b1, acc);
+      f32x16 aab = mfma32(f.a0, b0 & mask, zero);
+      aab = mfma32(f.a1, b1 & mask, aab);
+      bool cand = false;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float ak = fabsf(acc[r]);
+        cand |= aab[r] > 0.0f && ak + err_bound(aab[r], 0x1p-17f, ak) >= lo_wg;
+      }
+      const uint64_t c = __ballot(cand);
+      const uint32_t tokens = (uint32_t)c | (uint32_t)(c >> 32);  // token n: lane n or n + 32
+      const uint32_t tile = (uint32_t)(uintptr_t)(lds_cu8*)(L.xs[u] + wave * 64);
+      const XTile none = {b0, b1};
+      uint32_t pend = tokens;
+      while (pend) {
+        const int n = __builtin_ctz(pend);
+        exact_panel<true>(tile + n * kXRow, none, f, acc, L.y[wave], n, lane);
+        pend &= pend - 1;
+      }
+      if ((tokens >> (lane & 31)) & 1u) m = fmaxf(m, max_abs16(acc));
+    }
+  }
+  const float m_wg = block_max_nonneg(m, L.red[1], wave, lane);
+  if (threadIdx.x == 0 && m_wg > 0.0f) {
+    const uint32_t w = __float_as_uint(m_wg);
+    // The stored value only grows, so a stale read just costs an atomic.
+    if (w > __hip_atomic_load(a.amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(a.amax_bits, w);
   }
 }
 
@@ -646,37 +768,7 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
   __syncthreads();
 
   if (AMAX) {
-    // 3'. contract; the run's max |y|, one atomic per workgroup at most.
-    float m = 0.0f;
-    if (panel_ok) {
-      const uint8_t* row = L.xs[0] + (lane & 31) * kXRow + wave * 64 + 16 * (lane >> 5);
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) {
-        if (!FULL && u >= n_tiles) break;
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(row + u * (32 * kXRow));
-        const u32x4 b1 = *reinterpret_cast<const u32x4*>(row + u * (32 * kXRow) + 32);
-        f32x16 zero = {};
-        f32x16 acc = mfma32(f.t0, b0, zero);
-        acc = mfma32(f.t1, b1, acc);
-        m = fmaxf(m, max_abs16(acc));
-      }
-    }
-    uint32_t mb = __float_as_uint(m);  // non-negative floats order like their bit patterns
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const uint32_t v = (uint32_t)__shfl_xor((int)mb, o, 64);
-      mb = mb > v ? mb : v;
-    }
-    uint32_t* red = reinterpret_cast<uint32_t*>(L.y[0]);
-    if (lane == 0) red[wave] = mb;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t w = red[0];
-      for (int i = 1; i < kQWaves; ++i) w = w > red[i] ? w : red[i];
-      // The stored value only grows, so a stale read just costs an atomic.
-      if (w > __hip_atomic_load(a.amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-        atomicMax(a.amax_bits, w);
-    }
+    amax_run<FMT, TPW, FULL>(a, L, f, panel_ok, n_tiles, wave, lane);
     return;
   }
 
