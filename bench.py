@@ -40,25 +40,36 @@ MALL_BYTES = 256 << 20
 TRANSFORMS = ("wush", "wus", "hadamard", "identity")
 
 
-def build_bank(name, wl):
-    """bf16 transform bank [C][G][G] for a workload.  WUSH and WUS come from
-    the workload's weight and calibration statistics (product builder);
-    the blockwise Hadamard and the identity are the pages' data-agnostic
-    comparators (RTN-H and plain RTN)."""
+def workload_layer(wl, dev):
+    """The workload's weight and calibration activations as bf16 device
+    tensors (seeded synthetic data, rounded to bf16 by the generator)."""
+    import numpy as np
     import torch
 
+    from synthetic import f64_to_bf16_bits, gen_calibration, gen_weight
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    wb, xb = f64_to_bf16_bits(gen_weight(wl)), f64_to_bf16_bits(gen_calibration(wl))
+    return wb, xb, dev_bf16(wb), dev_bf16(xb)
+
+
+def build_bank(name, wl, dev):
+    """bf16 transform bank [C][G][G] on the device for a workload.  WUSH and
+    WUS come from the workload's weight and calibration statistics, built by
+    the library (wush_build_transforms); the blockwise Hadamard and the
+    identity are the pages' data-agnostic comparators (RTN-H and plain RTN,
+    wush_fixed_transforms)."""
     from mxfp4_activation_amd import transforms
-    from synthetic import gen_calibration, gen_weight
 
     C, G = wl.K // wl.G, wl.G
     if name in ("wush", "wus"):
-        T, _ = transforms.wush_transforms(torch.from_numpy(gen_weight(wl)), torch.from_numpy(gen_calibration(wl)), G,
-                                          use_hadamard=(name == "wush"))
-    elif name == "hadamard":
-        T = transforms.hadamard_transforms(C, G)
-    else:
-        T = transforms.identity_transforms(C, G)
-    return transforms.to_kernel_layout(T)
+        _, _, Wd, Xd = workload_layer(wl, dev)
+        return transforms.wush_bank(Wd, Xd, G, use_hadamard=(name == "wush"))[0]
+    if name == "hadamard":
+        return transforms.hadamard_bank(C, G, dev)
+    return transforms.identity_bank(C, G, dev)
 
 
 def algorithmic_bytes(fmt: str, M: int, K: int, G: int) -> int:
@@ -101,7 +112,7 @@ def parse():
                     help="layerwise loss (Eq. 5) of I / H / WUS / WUSH in MXFP4, NVFP4 and INT4 on synthetic "
                          "Qwen3-8B-shaped layers, computed by the kernels, instead of the headline measurement")
     ap.add_argument("--build-transforms", action="store_true",
-                    help="time the GPU transform construction (wush_build_transforms) against the torch float64 "
+                    help="time the GPU transform construction (wush_build_transforms) on each workload's layer, "
                          "builder on each workload's layer, instead of the headline measurement")
     ap.add_argument("--gptq-wush", action="store_true",
                     help="GPTQ-WUSH (Algorithm 1) on synthetic 4096-wide layers: calibration time on the GPU and the "
@@ -219,19 +230,38 @@ def ingest_traffic(args) -> None:
     print(json.dumps(out))
 
 
-def cpu_baseline(wl, x_bits_np, t_bits_np, seconds: float):
-    """The oracle as it stands, on the host cores, over whole passes of the
-    same workload until at least `seconds` have elapsed."""
+def cpu_baseline(wl, x_bits_np, transform: str, seconds: float):
+    """The oracle as it stands, on the host cores: first its construction of
+    the workload's transform bank (float64 Cholesky and SVD per block, timed
+    on its own), then whole passes of the online path over the same
+    activations until at least `seconds` have elapsed.  The oracle builds its
+    bank from the same bf16 weight and calibration values the library's
+    builder takes; nothing it computes comes from the GPU path."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
-    from oracle import quant
+    from oracle import codecs, quant
+    from oracle import transform as tr
 
     cores = len(os.sched_getaffinity(0))
-    g = None
-    passes = 0
-    t0 = time.perf_counter()
+    C, G = wl.K // wl.G, wl.G
+    t_build = None
     with threadpool_limits(limits=cores):
+        if transform in ("wush", "wus"):
+            wb, xb, _, _ = workload_layer(wl, "cpu")
+            W = codecs.bf16_bits_to_f32(wb).astype(np.float64)
+            Xc = codecs.bf16_bits_to_f32(xb).astype(np.float64)
+            tb0 = time.perf_counter()
+            T64, _ = tr.build_transforms(W, Xc, G, H=None if transform == "wush" else np.eye(G))
+            t_build = time.perf_counter() - tb0
+        elif transform == "hadamard":
+            T64 = np.broadcast_to(tr.hadamard(G), (C, G, G)).copy()
+        else:
+            T64 = np.broadcast_to(np.eye(G), (C, G, G)).copy()
+        t_bits_np = tr.transforms_to_bf16_bits(T64)
+        g = None
+        passes = 0
+        t0 = time.perf_counter()
         while True:
             if wl.fmt == "nvfp4" and g is None:
                 y = quant.transform_ref(x_bits_np, t_bits_np)
@@ -250,8 +280,7 @@ def cpu_baseline(wl, x_bits_np, t_bits_np, seconds: float):
                 break
     except OSError:
         pass
-    del np
-    return {
+    out = {
         "value": round(nbytes * passes / el / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
@@ -260,6 +289,12 @@ def cpu_baseline(wl, x_bits_np, t_bits_np, seconds: float):
                   "BLAS threads=%d, rest single-threaded; %s)" % (passes, wl.M, wl.K, el, cores, cpu_model),
         "elements_per_s": round(wl.M * wl.K * passes / el, 1),
     }
+    if t_build is not None:
+        out["transform_construction"] = {
+            "seconds": round(t_build, 3), "blocks": C, "G": G, "d_out": wl.d_out, "n_cal": wl.n_cal,
+            "what": "oracle build of the %s bank (moments, damping, Cholesky, SVD, products per block, "
+                    "float64), once, same host and threads" % transform}
+    return out
 
 
 def context_runs(graph_ms, launch, sets, n_sets, nbytes, M, K, dev):
@@ -298,7 +333,7 @@ def compare_transforms(args) -> None:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     X0 = torch.from_numpy(gen_x_bits(wl).view(np.int16)).view(torch.bfloat16).to(dev)
-    banks = {name: build_bank(name, wl).to(dev) for name in TRANSFORMS}
+    banks = {name: build_bank(name, wl, dev) for name in TRANSFORMS}
     nbytes = algorithmic_bytes(fmt, M, K, G)
     n_sets = args.sets or max(2, -(-2 * MALL_BYTES // nbytes) + 1)
     sdt = torch.float16 if fmt == "int4" else torch.uint8
@@ -394,14 +429,13 @@ def gemm_layers(args) -> None:
             x[:, out_ch] *= 30.0
             return x
         torch.manual_seed(K * 7 + N)
-        Xcal = acts(2048).double()
+        Xcal = acts(2048).to(torch.bfloat16).to(dev)
         W = (torch.randn(N, K, generator=gen, dtype=torch.float64) * 0.02)
-        Tw, Tx = transforms.wush_transforms(W, Xcal, G)
-        Hb = transforms.hadamard_transforms(C, G)
         X = acts(M).to(torch.bfloat16).to(dev)
         Wb = W.to(torch.bfloat16).to(dev)
-        banks = {"wush": (transforms.to_kernel_layout(Tw).to(dev), transforms.to_kernel_layout(Tx).to(dev)),
-                 "hadamard": (transforms.to_kernel_layout(Hb).to(dev),) * 2}
+        Tw, Tx, _, _ = transforms.wush_bank(Wb, Xcal, G)
+        Hb = transforms.hadamard_bank(C, G, dev)
+        banks = {"wush": (Tw, Tx), "hadamard": (Hb, Hb)}
         wq = {k: ops.quant("mxfp4", Wb, tb[1]) for k, tb in banks.items()}
         xc = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
         xs = torch.empty((M, K // G), dtype=torch.uint8, device=dev)
@@ -493,9 +527,10 @@ def layer_loss(args) -> None:
         W, Xc, Xe = gen_linear_layer(K, N, 2048, 2048, seed=7000 + li, n_outlier=max(1, K // 100))
         X, Wd = bf16(Xe), bf16(W)
         ref_ms = float((X.float() @ Wd.float().t()).double().pow(2).mean().item())
+        Xcd = bf16(Xc)
         for fmt in ("mxfp4", "nvfp4", "int4"):
             G = 16 if fmt == "nvfp4" else 32
-            banks = layerwise.transform_pairs(torch.from_numpy(W), torch.from_numpy(Xc), G, dev)
+            banks = layerwise.transform_pairs(Wd, Xcd, G)
             losses = {k: layerwise.layerwise_loss(fmt, X, Wd, a, b) for k, (a, b) in banks.items()}
             row = {"layer": name, "d_in": K, "d_out": N, "format": fmt,
                    "loss": {k: float("%.6g" % v) for k, v in losses.items()},
@@ -508,25 +543,23 @@ def layer_loss(args) -> None:
 
 def build_transforms_timing(args) -> None:
     """Offline construction of T_wush and T_xvsh for each workload's layer
-    (Eq. 7, Eq. 8): the GPU kernel (moments, damping, Cholesky, Jacobi SVD,
-    products, one workgroup per block, float64) against the torch float64
-    builder on the host (batched LAPACK), with the largest difference
-    between the two relative to each block's largest entry."""
+    (Eq. 7, Eq. 8) in the library: moments, damping, Cholesky, Jacobi SVD and
+    the products, one workgroup per block, float64 on the device.  Its
+    agreement with the oracle is a test (tests/test_gpu_build.py); the
+    oracle's own construction time on the host is part of the default
+    run's cpu_baseline."""
     import statistics
 
-    import numpy as np
     import torch
 
-    from mxfp4_activation_amd import ops, transforms
-    from synthetic import CONFIGS, f64_to_bf16_bits, gen_calibration, gen_weight
+    from mxfp4_activation_amd import ops
+    from synthetic import CONFIGS
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     for name in ("llama8b_mxfp4", "downproj_mxfp4", "nvfp4", "int4"):
         wl = CONFIGS[name]
-        W, Xc = gen_weight(wl), gen_calibration(wl)
-        Wd = torch.from_numpy(f64_to_bf16_bits(W).view(np.int16)).to(dev).view(torch.bfloat16)
-        Xd = torch.from_numpy(f64_to_bf16_bits(Xc).view(np.int16)).to(dev).view(torch.bfloat16)
+        _, _, Wd, Xd = workload_layer(wl, dev)
         for _ in range(2):
             ops.build_transforms(Wd, Xd, wl.G)
         torch.cuda.synchronize()
@@ -534,19 +567,12 @@ def build_transforms_timing(args) -> None:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for _ in range(5):
             e0.record()
-            tw, tx, _, _ = ops.build_transforms(Wd, Xd, wl.G)
+            ops.build_transforms(Wd, Xd, wl.G)
             e1.record()
             torch.cuda.synchronize()
             gpu.append(e0.elapsed_time(e1))
-        t0 = time.perf_counter()
-        rw, rx = transforms.wush_transforms(torch.from_numpy(W), torch.from_numpy(Xc), wl.G)
-        cpu_ms = (time.perf_counter() - t0) * 1e3
-        dev_err = max(float(((a.cpu() - b).abs().amax(dim=(1, 2)) / b.abs().amax(dim=(1, 2))).max())
-                      for a, b in ((tw, rw), (tx, rx)))
         print(json.dumps({"workload": name, "d_out": wl.d_out, "n_cal": wl.n_cal, "d_in": wl.K, "G": wl.G,
-                          "blocks": wl.K // wl.G, "gpu_ms": round(statistics.median(gpu), 3),
-                          "torch_cpu_float64_ms": round(cpu_ms, 1), "cpu_threads": torch.get_num_threads(),
-                          "max_rel_diff": float("%.3g" % dev_err)}), flush=True)
+                          "blocks": wl.K // wl.G, "gpu_ms": round(statistics.median(gpu), 3)}), flush=True)
 
 
 def gptq_wush_bench(args) -> None:
@@ -589,11 +615,12 @@ def gptq_wush_bench(args) -> None:
             torch.cuda.synchronize()
             key = "gptq_wush" if mode else "rtn_alg1"
             row[key + "_calib_s"] = round(time.perf_counter() - t0, 2)
-            row[key + "_rel_err"] = float("%.5g" % forward(transforms.to_kernel_layout(r.T_x.cpu()).to(dev),
-                                                           r.codes, r.scales))
-        Tw, Tx = transforms.wush_transforms(torch.from_numpy(W), torch.from_numpy(Xc), 32)
-        wq_c, wq_s = ops.quant("mxfp4", Wd.to(torch.bfloat16), transforms.to_kernel_layout(Tx).to(dev))
-        row["rtn_eq8_rel_err"] = float("%.5g" % forward(transforms.to_kernel_layout(Tw).to(dev), wq_c, wq_s))
+            row[key + "_rel_err"] = float("%.5g" % forward(transforms.to_kernel_layout(r.T_x), r.codes, r.scales))
+        Wb = torch.from_numpy(f64_to_bf16_bits(W).view(np.int16)).to(dev).view(torch.bfloat16)
+        Xcb = torch.from_numpy(f64_to_bf16_bits(Xc).view(np.int16)).to(dev).view(torch.bfloat16)
+        Tw, Tx, _, _ = transforms.wush_bank(Wb, Xcb, 32)
+        wq_c, wq_s = ops.quant("mxfp4", Wb, Tx)
+        row["rtn_eq8_rel_err"] = float("%.5g" % forward(Tw, wq_c, wq_s))
         print(json.dumps(row), flush=True)
 
 
@@ -632,8 +659,8 @@ def main():
     import torch
 
     import mxfp4_activation_amd as wush
-    from mxfp4_activation_amd import _lib, transforms
-    from synthetic import CONFIGS, gen_calibration, gen_weight, gen_x_bits
+    from mxfp4_activation_amd import _lib
+    from synthetic import CONFIGS, gen_x_bits
 
     wl = CONFIGS[args.workload]
     M, K, G, fmt = wl.M, wl.K, wl.G, wl.fmt
@@ -644,10 +671,8 @@ def main():
 
     # Inputs: seeded activations and the offline transform bank.
     x_np = gen_x_bits(wl)
-    T_bf16 = build_bank(args.transform, wl)
-    t_np = T_bf16.view(torch.int16).numpy().view(np.uint16)
+    T0 = build_bank(args.transform, wl, dev)
     X0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
-    T0 = T_bf16.to(dev)
 
     nbytes = algorithmic_bytes(fmt, M, K, G)
     per_set = nbytes
@@ -847,7 +872,7 @@ def main():
         out["context"]["nvfp4_with_absmax_prepass"] = prepass
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle (~%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, x_np, t_np, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, x_np, args.transform, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

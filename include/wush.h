@@ -32,17 +32,25 @@
  *           block c, so block c's matrix is one contiguous G*G slice.
  *           16-byte aligned.
  *   codes   uint8 [M][K/2].  Element 2j in bits 3:0 of byte j, element 2j+1
- *           in bits 7:4.  8-byte aligned.
- *   scales  one per (token, block), [M][K/G].  The format decides the type.
+ *           in bits 7:4.  16-byte aligned.
+ *   scales  one per (token, block), [M][K/G].  The format decides the type
+ *           and the alignment (8 bytes for MXFP4, 16 for NVFP4 and INT4).
+ *   The kernels write codes and scales with 16- and 8-byte vector stores,
+ *   which these alignments keep on natural boundaries.
  *
  * Pre-quantization values: y = fp32 rounding of the exact sum
  * sum_j T[c][i][j] * x_j.  The kernels use fp32 matrix-core accumulation,
  * which can differ from the exact sum by an error bounded by the sum of
  * |T x| terms.  Any group whose scale decision falls within that bound of
- * a rounding boundary is recomputed in float64.  So every scale equals the
- * one computed from the exactly rounded y.  An element code may still differ
- * by one level where the scaled value sits within that bound of a rounding
- * midpoint.
+ * a rounding boundary is recomputed: the G products (each exact in
+ * float64) are summed in float64 and rounded once to fp32.  That sum is
+ * exact when the products span at most 32 binary octaves; beyond that its
+ * error stays below 2^-47 of the sum of |T x| terms, so the recomputed y
+ * can differ from the exactly rounded one only if the exact sum lies that
+ * close to an fp32 rounding midpoint.  With that proviso every scale equals
+ * the one computed from the exactly rounded y.  An element code may still
+ * differ by one level where the scaled value sits within the accumulation
+ * bound of a rounding midpoint.
  */
 #ifndef WUSH_H_
 #define WUSH_H_
@@ -55,7 +63,7 @@
 extern "C" {
 #endif
 
-#define WUSH_ABI_VERSION 1
+#define WUSH_ABI_VERSION 2
 
 typedef enum wush_status {
   WUSH_OK = 0,
@@ -70,7 +78,7 @@ typedef enum wush_status {
  * clamped to [-127, 127], and amax = 0 gives code 0.  Elements are y * 2^-e.
  * MXFP4 is E2M1 elements with a shared 8-bit scale per 32 (deep dive,
  * section 2, "New block-level floating-point formats"; OCP MX v1.0).
- * scales: uint8 [M][K/32].  K must be a multiple of 32. */
+ * scales: uint8 [M][K/32], 8-byte aligned.  K must be a multiple of 32. */
 wush_status wush_quant_mxfp4(const void* X, const void* T, int64_t M, int64_t K,
                              void* codes, void* scales, hipStream_t stream);
 
@@ -81,8 +89,9 @@ wush_status wush_quant_mxfp4(const void* X, const void* T, int64_t M, int64_t K,
  * If g == 0 or eff == 0, the group's codes are all zero.  Pass the g from
  * wush_nvfp4_global_scale (dynamic) or a calibrated constant (static).  g
  * must be 0 or at least 2^-100.  NVFP4 is E2M1 with an FP8 scale per 16 (deep
- * dive, section 2).
- * scales: uint8 [M][K/16].  K must be a multiple of 16. */
+ * dive, section 2).  The pages do not say how g is chosen; this interface
+ * takes it from device memory, so it can be dynamic or calibrated.
+ * scales: uint8 [M][K/16], 16-byte aligned.  K must be a multiple of 16. */
 wush_status wush_quant_nvfp4(const void* X, const void* T, int64_t M, int64_t K,
                              const float* global_scale, void* codes, void* scales,
                              hipStream_t stream);
@@ -91,11 +100,12 @@ wush_status wush_quant_nvfp4(const void* X, const void* T, int64_t M, int64_t K,
  * One IEEE fp16 scale per 32: s = fp16(fp32(amax / 7)).  Elements are
  * rne(clamp(y * fp32(1/s), -7, 7)), and s == 0 gives zero codes.  This is
  * the AbsMax INT quantizer (deep dive, section 3.4.5).
- * scales: fp16 bits [M][K/32], 2-byte aligned.  K must be a multiple of 32. */
+ * scales: fp16 bits [M][K/32], 16-byte aligned.  K must be a multiple of 32. */
 wush_status wush_quant_int4(const void* X, const void* T, int64_t M, int64_t K,
                             void* codes, void* scales, hipStream_t stream);
 
-/* Generic form of the three entry points above.
+/* Generic form of the three entry points above (an interface of this
+ * library; the pages define no API).
  * fmt: 0 = MXFP4, 1 = NVFP4, 2 = INT4.
  * global_scale: used only for NVFP4.
  * n_exact: if non-null, a device uint32 to which the kernel atomically adds
@@ -188,32 +198,61 @@ wush_status wush_gptq_block(int fmt, const double* Wbar, const double* R, int G,
 /* Transform only: Y[m][cG+i] = sum_j T[c][i][j] x_(cG+j), in fp32 from the
  * matrix cores, without rounding fix-up.  G is 16 or 32.  Use it to check
  * values before quantization, or when the transformed activations are wanted
- * in fp32.
+ * in fp32.  The product is the block transform of Eq. 8 applied to the
+ * activations (deep dive, section 3.4.4); the pages define no such entry,
+ * since their kernel never writes the transformed values out.
  * Y: fp32 [M][K], 16-byte aligned. */
 wush_status wush_transform_f32(const void* X, const void* T, int64_t M, int64_t K, int G,
                                float* Y, hipStream_t stream);
 
-/* Largest |y| over the whole transformed tensor (fp32, matrix-core values:
- * within 2^-17 * max_k sum_j |T_kj x_j| + 2^-21 * amax of the exact
- * maximum).  *amax is overwritten, not accumulated: the call enqueues a
- * fill of *amax with 0, then the pass, which folds each workgroup's maximum
- * in with an atomic max.  Two calls that share `amax` on different streams
- * race.  G is 16 or 32. */
-wush_status wush_transformed_absmax(const void* X, const void* T, int64_t M, int64_t K, int G,
+/* Largest |y| over the whole transformed tensor, where y is the exactly
+ * rounded fp32 value of each output (the same y the quantizers' scales
+ * use).  The pass bounds every matrix-core value by its accumulation
+ * error and recomputes, in float64, only the tokens that can hold the
+ * maximum, so the result is the maximum of the recomputed values.
+ * The pages do not define this entry: it serves the NVFP4 per-tensor scale,
+ * which they leave open (see wush_nvfp4_global_scale).
+ * *amax is overwritten, not accumulated: the call enqueues a fill of *amax
+ * with 0, then the pass, which folds each workgroup's maximum in with an
+ * atomic max.  Two calls that share `amax` on different streams race.
+ * G is 16 or 32.  amax: device fp32, 4-byte aligned. */
+wush_status wush_absmax_transformed(const void* X, const void* T, int64_t M, int64_t K, int G,
                                     float* amax, hipStream_t stream);
 
 /* NVFP4 per-tensor scale: *global_scale = fp32(absmax(T x) / 2688), with
- * 2688 = 6 * 448.  The block holding the tensor maximum then gets the
- * largest E4M3 scale.  G = 16. */
+ * 2688 = 6 * 448 and absmax from wush_absmax_transformed (G = 16).  The
+ * block holding the tensor maximum then gets the largest E4M3 scale.  The
+ * pages name NVFP4's FP8 block scale but not its tensor scale; this
+ * dynamic AbsMax rule is this library's reading. */
 wush_status wush_nvfp4_global_scale(const void* X, const void* T, int64_t M, int64_t K,
                                     float* global_scale, hipStream_t stream);
 
 /* The E2M1 element rounding the kernels use, exposed for exhaustive testing:
  * codes[i] = E2M1_rne_sat(v[i]), one 4-bit code per byte, sign in bit 3.
- * n >= 0.  v is fp32, 4-byte aligned. */
+ * n >= 0.  v is fp32, 4-byte aligned.  A test interface of this library:
+ * the pages name the E2M1 element format (deep dive, section 2) but define
+ * no entry point. */
 wush_status wush_e2m1_encode(const float* v, int64_t n, uint8_t* codes, hipStream_t stream);
 
-/* Status text, and the detail of the last failure on this thread. */
+/* Fixed transform banks, the data-agnostic comparators the pages evaluate
+ * through the same quantizer (deep dive, section 5: RTN with no transform,
+ * and RTN-H, the blockwise Hadamard transform):
+ *   kind 0: T[c] = I;  kind 1: T[c] = H / sqrt(G), H the Sylvester Hadamard
+ *   matrix (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]), for c < C.
+ * G is 16 or 32; C >= 0 (0 is a no-op).  Outputs (either may be NULL, not
+ * both): T float64 [C][G][G], 8-byte aligned; T_bf16 bf16 [C][G][G] in the
+ * kernel layout (bf16 of fp32 of the value), 16-byte aligned. */
+wush_status wush_fixed_transforms(int kind, int64_t C, int G, double* T, void* T_bf16, hipStream_t stream);
+
+/* The kernel layout of a float64 transform bank: dst[i] = bf16(fp32(src[i]))
+ * (both roundings to nearest even), the 16-bit storage of T the pages
+ * describe (ai.info summary: transforms kept in 16 bits; deep dive,
+ * section 3.4.7: BF16 or FP16 transform matrices).  n >= 0; src 8-byte
+ * aligned, dst 2-byte aligned; they must not overlap. */
+wush_status wush_f64_to_bf16(const double* src, int64_t n, void* dst, hipStream_t stream);
+
+/* Status text, and the detail of the last failure on this thread.  Library
+ * interfaces; nothing on the pages corresponds. */
 const char* wush_status_string(wush_status status);
 const char* wush_last_error(void);
 int wush_abi_version(void);

@@ -28,7 +28,9 @@ SIGNATURES = {
     "wush_build_transforms": (_c_int, [_vp, _i64, _vp, _i64, _i64, _c_int, ctypes.c_double, _c_int, _vp, _vp, _vp,
                                        _vp, _vp]),
     "wush_transform_f32": (_c_int, [_vp, _vp, _i64, _i64, _c_int, _vp, _vp]),
-    "wush_transformed_absmax": (_c_int, [_vp, _vp, _i64, _i64, _c_int, _vp, _vp]),
+    "wush_absmax_transformed": (_c_int, [_vp, _vp, _i64, _i64, _c_int, _vp, _vp]),
+    "wush_fixed_transforms": (_c_int, [_c_int, _i64, _c_int, _vp, _vp, _vp]),
+    "wush_f64_to_bf16": (_c_int, [_vp, _i64, _vp, _vp]),
     "wush_nvfp4_global_scale": (_c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
     "wush_e2m1_encode": (_c_int, [_vp, _i64, _vp, _vp]),
     "wush_status_string": (ctypes.c_char_p, [_c_int]),
@@ -36,7 +38,7 @@ SIGNATURES = {
     "wush_abi_version": (_c_int, []),
 }
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class WushError(RuntimeError):

@@ -164,9 +164,12 @@ wush_status wush_quant(int fmt, const void* X, const void* T, int64_t M, int64_t
   if (st != WUSH_OK || M == 0) return st;
   if (!codes || !scales) return fail(WUSH_EINVAL, "null codes or scales");
   if (fmt == wush::kNVFP4 && !global_scale) return fail(WUSH_EINVAL, "NVFP4 needs global_scale");
-  if (!aligned(codes, 8)) return fail(WUSH_EALIGN, "codes must be 8-byte aligned");
+  // The kernels store codes in 16-byte vectors and each row's scales in
+  // 8-byte (MXFP4) or 16-byte (NVFP4, INT4) vectors.
+  if (!aligned(codes, 16)) return fail(WUSH_EALIGN, "codes must be 16-byte aligned");
   const int scale_bytes = (fmt == wush::kINT4) ? 2 : 1;
-  if (!aligned(scales, scale_bytes)) return fail(WUSH_EALIGN, "scales must be %d-byte aligned", scale_bytes);
+  const int scale_align = (fmt == wush::kMXFP4) ? 8 : 16;
+  if (!aligned(scales, scale_align)) return fail(WUSH_EALIGN, "scales must be %d-byte aligned", scale_align);
   if (global_scale && fmt == wush::kNVFP4 && !aligned(global_scale, 4))
     return fail(WUSH_EALIGN, "global_scale must be 4-byte aligned");
   if (n_exact && !aligned(n_exact, 4)) return fail(WUSH_EALIGN, "n_exact must be 4-byte aligned");
@@ -276,7 +279,7 @@ static wush_status absmax_common(const void* X, const void* T, int64_t M, int64_
   return WUSH_OK;
 }
 
-wush_status wush_transformed_absmax(const void* X, const void* T, int64_t M, int64_t K, int G,
+wush_status wush_absmax_transformed(const void* X, const void* T, int64_t M, int64_t K, int G,
                                     float* amax, hipStream_t stream) {
   g_last_error[0] = 0;
   return absmax_common(X, T, M, K, G, amax, stream);
@@ -435,6 +438,40 @@ wush_status wush_gptq_block(int fmt, const double* Wbar, const double* R, int G,
   a.scales = scales;
   a.scales_stride = scales_stride;
   hipError_t e = wush::launch_gptq_block(fmt, G, a, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+wush_status wush_fixed_transforms(int kind, int64_t C, int G, double* T, void* T_bf16, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (kind != 0 && kind != 1) return fail(WUSH_EINVAL, "kind must be 0 (identity) or 1 (Hadamard), got %d", kind);
+  if (G != 16 && G != 32) return fail(WUSH_EUNSUPPORTED, "G must be 16 or 32 (got %d)", G);
+  if (C < 0) return fail(WUSH_EINVAL, "C must be >= 0");
+  if (C > ((int64_t)1 << 31) / (G * G)) return fail(WUSH_EINVAL, "C too large");
+  if (!T && !T_bf16) return fail(WUSH_EINVAL, "both outputs are null");
+  if (C == 0) return WUSH_OK;
+  if (T && !aligned(T, 8)) return fail(WUSH_EALIGN, "T must be 8-byte aligned");
+  if (T_bf16 && !aligned(T_bf16, 16)) return fail(WUSH_EALIGN, "T_bf16 must be 16-byte aligned");
+  const uint64_t n = (uint64_t)C * G * G;
+  if (T && T_bf16 && overlap(T, n * 8, T_bf16, n * 2)) return fail(WUSH_EINVAL, "outputs overlap");
+  wush_status st = check_device();
+  if (st != WUSH_OK) return st;
+  hipError_t e = wush::launch_fixed(kind, C, G, T, static_cast<uint16_t*>(T_bf16), stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+wush_status wush_f64_to_bf16(const double* src, int64_t n, void* dst, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (n < 0) return fail(WUSH_EINVAL, "n must be >= 0");
+  if (n == 0) return WUSH_OK;
+  if (n > ((int64_t)1 << 40)) return fail(WUSH_EINVAL, "n too large");
+  if (!src || !dst) return fail(WUSH_EINVAL, "null pointer");
+  if (!aligned(src, 8) || !aligned(dst, 2)) return fail(WUSH_EALIGN, "src must be 8-byte and dst 2-byte aligned");
+  if (overlap(src, (uint64_t)n * 8, dst, (uint64_t)n * 2)) return fail(WUSH_EINVAL, "dst overlaps src");
+  wush_status st = check_device();
+  if (st != WUSH_OK) return st;
+  hipError_t e = wush::launch_f64_to_bf16(src, n, static_cast<uint16_t*>(dst), stream);
   if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
   return WUSH_OK;
 }

@@ -20,4 +20,11 @@ struct BuildArgs {
 // G is 16 or 32; the caller has validated sizes, alignment and overlap.
 hipError_t launch_build(int G, const BuildArgs& a, hipStream_t s);
 
+// Fixed banks: kind 0 = identity, 1 = normalized Sylvester Hadamard, C
+// copies, into float64 and/or bf16 outputs (either may be null).
+hipError_t launch_fixed(int kind, int64_t C, int G, double* T, uint16_t* T_bf16, hipStream_t s);
+
+// dst[i] = bf16(fp32(src[i])), i < n.
+hipError_t launch_f64_to_bf16(const double* src, int64_t n, uint16_t* dst, hipStream_t s);
+
 }  // namespace wush

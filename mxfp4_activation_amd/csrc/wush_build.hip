@@ -276,7 +276,40 @@ __global__ __launch_bounds__(kThreads) void build_kernel(BuildArgs a) {
   }
 }
 
+// One thread per entry of the bank: identity (kind 0) or the normalized
+// Sylvester Hadamard matrix (kind 1), the same in every block.
+template <int G>
+__global__ void fixed_kernel(int kind, int64_t n, double* T, uint16_t* T_bf16) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const int i = (int)((e / G) % G), j = (int)(e % G);
+  const double v = kind ? hadamard<G>(i, j) : (i == j ? 1.0 : 0.0);
+  if (T) T[e] = v;
+  if (T_bf16) T_bf16[e] = f64_to_bf16_via_f32(v);
+}
+
+__global__ void f64_to_bf16_kernel(const double* __restrict__ src, int64_t n, uint16_t* __restrict__ dst) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = f64_to_bf16_via_f32(src[i]);
+}
+
 }  // namespace
+
+hipError_t launch_f64_to_bf16(const double* src, int64_t n, uint16_t* dst, hipStream_t s) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(f64_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, n, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_fixed(int kind, int64_t C, int G, double* T, uint16_t* T_bf16, hipStream_t s) {
+  const int64_t n = C * G * G;
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (G == 32) hipLaunchKernelGGL((fixed_kernel<32>), grid, block, 0, s, kind, n, T, T_bf16);
+  else hipLaunchKernelGGL((fixed_kernel<16>), grid, block, 0, s, kind, n, T, T_bf16);
+  return hipGetLastError();
+}
 
 hipError_t launch_build(int G, const BuildArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.d_in / G)), block(kThreads);

@@ -31,7 +31,7 @@ import torch
 
 from . import _lib
 from .ops import _stream
-from .transforms import hadamard
+from .transforms import hadamard_f64
 
 DEFAULT_GPTQ_DAMP = 0.01
 
@@ -61,7 +61,7 @@ def gptq_wush(W: torch.Tensor, Xcal: torch.Tensor, G: int, fmt: str, gptq: bool 
     Hx += damp * torch.diagonal(Hx).mean() * torch.eye(d_in, dtype=torch.float64, device=dev)
     Xp = torch.linalg.cholesky(Hx)
     Y = W @ Xp
-    Hd = hadamard(G, device=dev)
+    Hd = hadamard_f64(G, dev)
     eye = torch.eye(G, dtype=torch.float64, device=dev)
     T_x = torch.empty((C, G, G), dtype=torch.float64, device=dev)
     Wq = torch.empty((d_out, d_in), dtype=torch.float64, device=dev)

@@ -25,16 +25,16 @@ from . import ops, transforms
 TRANSFORM_PAIRS = ("I", "H", "WUS", "WUSH")
 
 
-def transform_pairs(W: torch.Tensor, Xcal: torch.Tensor, G: int, device) -> Dict[str, Tuple[torch.Tensor, torch.Tensor]]:
-    """bf16 kernel-layout banks (activation side, weight side) for each pair."""
+def transform_pairs(W: torch.Tensor, Xcal: torch.Tensor, G: int) -> Dict[str, Tuple[torch.Tensor, torch.Tensor]]:
+    """bf16 kernel-layout banks (activation side, weight side) for each pair,
+    built by the library from a bf16 device weight W [d_out, d_in] and bf16
+    device calibration activations Xcal [n_cal, d_in]."""
     C = W.shape[1] // G
-    wush_a, wush_w = transforms.wush_transforms(W, Xcal, G)
-    wus_a, wus_w = transforms.wush_transforms(W, Xcal, G, use_hadamard=False)
-    eye = transforms.identity_transforms(C, G)
-    had = transforms.hadamard_transforms(C, G)
-    pairs = {"I": (eye, eye), "H": (had, had), "WUS": (wus_a, wus_w), "WUSH": (wush_a, wush_w)}
-    return {k: (transforms.to_kernel_layout(a).to(device), transforms.to_kernel_layout(b).to(device))
-            for k, (a, b) in pairs.items()}
+    wush_a, wush_w, _, _ = transforms.wush_bank(W, Xcal, G)
+    wus_a, wus_w, _, _ = transforms.wush_bank(W, Xcal, G, use_hadamard=False)
+    eye = transforms.identity_bank(C, G, W.device)
+    had = transforms.hadamard_bank(C, G, W.device)
+    return {"I": (eye, eye), "H": (had, had), "WUS": (wus_a, wus_w), "WUSH": (wush_a, wush_w)}
 
 
 def quantize(fmt: str, X: torch.Tensor, bank: torch.Tensor):

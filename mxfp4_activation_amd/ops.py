@@ -35,6 +35,21 @@ def _check_x_t(X: torch.Tensor, T: torch.Tensor, G: int) -> Tuple[int, int]:
     return M, K
 
 
+def _check_buf(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> None:
+    """A caller-supplied buffer must be a contiguous device tensor of exactly
+    this dtype and shape on the inputs' device."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s must be on %s (got %s)" % (name, device, t.device))
+
+
 def quant(fmt: str, X: torch.Tensor, T: torch.Tensor, global_scale: Optional[torch.Tensor] = None,
           codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
           n_exact: Optional[torch.Tensor] = None):
@@ -42,23 +57,23 @@ def quant(fmt: str, X: torch.Tensor, T: torch.Tensor, global_scale: Optional[tor
     G = _G[fmt]
     M, K = _check_x_t(X, T, G)
     dev = X.device
+    sdt = torch.float16 if fmt == "int4" else torch.uint8
     if codes is None:
         codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     if scales is None:
-        sdt = torch.float16 if fmt == "int4" else torch.uint8
         scales = torch.empty((M, K // G), dtype=sdt, device=dev)
-    for t, shape in ((codes, (M, K // 2)), (scales, (M, K // G))):
-        if tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
-            raise ValueError("output buffer has the wrong shape, layout or device")
+    _check_buf(codes, "codes", torch.uint8, (M, K // 2), dev)
+    _check_buf(scales, "scales", sdt, (M, K // G), dev)
     gs = 0
     if fmt == "nvfp4":
-        if global_scale is None or global_scale.dtype != torch.float32 or global_scale.numel() != 1:
+        if global_scale is None:
             raise ValueError("nvfp4 needs a 1-element float32 global_scale tensor")
+        _check_buf(global_scale.view(-1) if global_scale.dim() else global_scale.view(1), "global_scale",
+                   torch.float32, (1,), dev)
         gs = global_scale.data_ptr()
     ne = 0
     if n_exact is not None:
-        if n_exact.dtype != torch.int32 or n_exact.numel() != 1:
-            raise ValueError("n_exact must be a 1-element int32 tensor")
+        _check_buf(n_exact.view(-1) if n_exact.dim() else n_exact.view(1), "n_exact", torch.int32, (1,), dev)
         ne = n_exact.data_ptr()
     lib = _lib.load()
     st = lib.wush_quant(_lib.FMT[fmt], X.data_ptr(), T.data_ptr(), M, K, gs or None, codes.data_ptr(),
@@ -157,20 +172,24 @@ def transform_f32(X: torch.Tensor, T: torch.Tensor, Y: Optional[torch.Tensor] = 
     M, K = _check_x_t(X, T, G)
     if Y is None:
         Y = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    _check_buf(Y, "Y", torch.float32, (M, K), X.device)
     lib = _lib.load()
     _lib.check(lib.wush_transform_f32(X.data_ptr(), T.data_ptr(), M, K, G, Y.data_ptr(), _stream()),
                "wush_transform_f32")
     return Y
 
 
-def transformed_absmax(X: torch.Tensor, T: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+def absmax_transformed(X: torch.Tensor, T: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Largest |y| of the exactly rounded transform over the whole tensor, as
+    a one-element fp32 device tensor."""
     G = T.shape[-1]
     M, K = _check_x_t(X, T, G)
     if out is None:
         out = torch.empty((1,), dtype=torch.float32, device=X.device)
+    _check_buf(out, "out", torch.float32, (1,), X.device)
     lib = _lib.load()
-    _lib.check(lib.wush_transformed_absmax(X.data_ptr(), T.data_ptr(), M, K, G, out.data_ptr(), _stream()),
-               "wush_transformed_absmax")
+    _lib.check(lib.wush_absmax_transformed(X.data_ptr(), T.data_ptr(), M, K, G, out.data_ptr(), _stream()),
+               "wush_absmax_transformed")
     return out
 
 
@@ -178,6 +197,7 @@ def nvfp4_global_scale(X: torch.Tensor, T: torch.Tensor, out: Optional[torch.Ten
     M, K = _check_x_t(X, T, 16)
     if out is None:
         out = torch.empty((1,), dtype=torch.float32, device=X.device)
+    _check_buf(out, "out", torch.float32, (1,), X.device)
     lib = _lib.load()
     _lib.check(lib.wush_nvfp4_global_scale(X.data_ptr(), T.data_ptr(), M, K, out.data_ptr(), _stream()),
                "wush_nvfp4_global_scale")
@@ -189,6 +209,34 @@ def e2m1_encode(v: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Te
         raise ValueError("v must be a contiguous float32 device tensor")
     if out is None:
         out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check_buf(out, "out", torch.uint8, v.shape, v.device)
     lib = _lib.load()
     _lib.check(lib.wush_e2m1_encode(v.data_ptr(), v.numel(), out.data_ptr(), _stream()), "wush_e2m1_encode")
+    return out
+
+
+def fixed_transforms(kind: str, C: int, G: int, device, f64: bool = False):
+    """Identity ("identity") or normalized Sylvester Hadamard ("hadamard")
+    bank [C, G, G], built by the library on the device: the bf16 kernel
+    layout, or float64 with f64=True."""
+    kinds = {"identity": 0, "hadamard": 1}
+    if kind not in kinds:
+        raise ValueError("kind must be 'identity' or 'hadamard'")
+    dt = torch.float64 if f64 else torch.bfloat16
+    out = torch.empty((C, G, G), dtype=dt, device=device)
+    lib = _lib.load()
+    _lib.check(lib.wush_fixed_transforms(kinds[kind], C, G, out.data_ptr() if f64 else None,
+                                         None if f64 else out.data_ptr(), _stream()), "wush_fixed_transforms")
+    return out
+
+
+def f64_to_bf16(T: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16(fp32(T)) of a float64 device tensor (the kernel layout of a bank)."""
+    if T.dtype != torch.float64 or not T.is_cuda or not T.is_contiguous():
+        raise ValueError("T must be a contiguous float64 device tensor")
+    if out is None:
+        out = torch.empty(T.shape, dtype=torch.bfloat16, device=T.device)
+    _check_buf(out, "out", torch.bfloat16, T.shape, T.device)
+    lib = _lib.load()
+    _lib.check(lib.wush_f64_to_bf16(T.data_ptr(), T.numel(), out.data_ptr(), _stream()), "wush_f64_to_bf16")
     return out

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, "binding lacks " + name
     assert set(_lib.SIGNATURES) == set(decl)
-    assert lib.wush_abi_version() == 1
+    assert lib.wush_abi_version() == _lib.ABI_VERSION == 2
 
 
 def test_status_strings():
@@ -55,6 +55,10 @@ def test_validation_rejects_bad_arguments(fmt):
     assert q(A + 2, A * 2, 8, G, A * 3, A * 4) == _lib.WUSH_EALIGN
     assert q(A, A * 2 + 8, 8, G, A * 3, A * 4) == _lib.WUSH_EALIGN
     assert q(A, A * 2, 8, G, A * 3 + 4, A * 4) == _lib.WUSH_EALIGN
+    assert q(A, A * 2, 8, G, A * 3 + 8, A * 4) == _lib.WUSH_EALIGN  # codes need 16 bytes
+    assert q(A, A * 2, 8, G, A * 3, A * 4 + 4) == _lib.WUSH_EALIGN  # scales need at least 8
+    if fmt != 0:
+        assert q(A, A * 2, 8, G, A * 3, A * 4 + 8) == _lib.WUSH_EALIGN  # NVFP4 and INT4 scales need 16
     # codes overlapping X
     assert q(A, A * 8, 8, 4 * G, A + 64, A * 16) == _lib.WUSH_EINVAL
     if fmt == 1:
@@ -145,3 +149,46 @@ def test_gptq_block_validation():
     assert g(0, 32, 8, cs=18) == _lib.WUSH_EALIGN
     assert g(0, 32, 8, c=B * 3 + 2) == _lib.WUSH_EALIGN
     assert g(0, 32, 8, c=B) == _lib.WUSH_EINVAL  # codes overlap Q
+
+
+def test_support_entry_validation():
+    lib = wush.load()
+    B = A * 64
+    assert lib.wush_absmax_transformed(A, A * 2, 8, 64, 24, B, None) == _lib.WUSH_EUNSUPPORTED
+    assert lib.wush_absmax_transformed(A, A * 2, 8, 64, 32, None, None) == _lib.WUSH_EINVAL
+    assert lib.wush_absmax_transformed(A, A * 2, 8, 64, 32, B + 2, None) == _lib.WUSH_EALIGN
+    assert lib.wush_nvfp4_global_scale(A, A * 2, 8, 40, B, None) == _lib.WUSH_EINVAL
+    assert lib.wush_transform_f32(A, A * 2, 8, 64, 32, B + 4, None) == _lib.WUSH_EALIGN
+    assert lib.wush_fixed_transforms(2, 4, 32, B, None, None) == _lib.WUSH_EINVAL
+    assert lib.wush_fixed_transforms(1, 4, 8, B, None, None) == _lib.WUSH_EUNSUPPORTED
+    assert lib.wush_fixed_transforms(1, 4, 32, None, None, None) == _lib.WUSH_EINVAL
+    assert lib.wush_fixed_transforms(1, 4, 32, None, B + 8, None) == _lib.WUSH_EALIGN
+    assert lib.wush_fixed_transforms(0, 0, 32, B, None, None) == _lib.WUSH_OK
+    assert lib.wush_f64_to_bf16(A, -1, B, None) == _lib.WUSH_EINVAL
+    assert lib.wush_f64_to_bf16(A + 4, 8, B, None) == _lib.WUSH_EALIGN
+    assert lib.wush_f64_to_bf16(A, 8, A + 8, None) == _lib.WUSH_EINVAL
+    assert lib.wush_f64_to_bf16(A, 0, None, None) == _lib.WUSH_OK
+
+
+def test_binding_checks_caller_buffers():
+    """The binding's buffer check (used for every caller-supplied output and
+    for global_scale / n_exact) rejects wrong dtype, shape, layout and device
+    before the library is called."""
+    torch = pytest.importorskip("torch")
+    from mxfp4_activation_amd.ops import _check_buf
+
+    dev = torch.device("cpu")
+    ok = torch.empty((4, 8), dtype=torch.uint8)
+    _check_buf(ok, "codes", torch.uint8, (4, 8), dev)
+    with pytest.raises(TypeError, match="codes must be torch.uint8"):
+        _check_buf(ok.view(torch.int8), "codes", torch.uint8, (4, 8), dev)
+    with pytest.raises(TypeError, match="scales must be torch.float16"):
+        _check_buf(torch.empty((4, 2), dtype=torch.uint8), "scales", torch.float16, (4, 1), dev)
+    with pytest.raises(ValueError, match="shape"):
+        _check_buf(ok, "codes", torch.uint8, (4, 9), dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        _check_buf(torch.empty((8, 4), dtype=torch.uint8).t(), "codes", torch.uint8, (4, 8), dev)
+    with pytest.raises(ValueError, match="must be on"):
+        _check_buf(ok, "codes", torch.uint8, (4, 8), torch.device("cuda", 0))
+    with pytest.raises(TypeError):
+        _check_buf(None, "out", torch.float32, (1,), dev)
