@@ -37,9 +37,8 @@ def x_rows(name: str, lo: int, hi: int, M: int = 0) -> np.ndarray:
 
 
 @functools.lru_cache(maxsize=None)
-def oracle_global_scale(name: str) -> np.float32:
-    """NVFP4 tensor scale from the oracle's AbsMax of the whole transformed
-    tensor, computed in row chunks."""
+def oracle_tensor_amax(name: str) -> np.float32:
+    """The oracle's AbsMax of the whole transformed tensor, in row chunks."""
     from oracle import quant
 
     _, tb = transforms(name)
@@ -47,7 +46,14 @@ def oracle_global_scale(name: str) -> np.float32:
     amax = np.float32(0.0)
     for lo in range(0, xb.shape[0], 4096):
         amax = max(amax, quant.tensor_amax_ref(quant.transform_ref(xb[lo:lo + 4096], tb)))
-    return quant.nvfp4_global_scale(amax)
+    return np.float32(amax)
+
+
+def oracle_global_scale(name: str) -> np.float32:
+    """NVFP4 tensor scale from the oracle's AbsMax of the whole tensor."""
+    from oracle import quant
+
+    return quant.nvfp4_global_scale(oracle_tensor_amax(name))
 
 
 def sample_rows(M: int, n_edge: int = 48, n_rand: int = 160, seed: int = 0) -> np.ndarray:

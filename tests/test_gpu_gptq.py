@@ -106,7 +106,7 @@ def test_eq10_forward_with_gptq_weights():
     err = {}
     for mode in (True, False):
         r = pg.gptq_wush(Wd, Xcd, 32, "mxfp4", gptq=mode)
-        bank = transforms.to_kernel_layout(r.T_x.cpu()).cuda()
+        bank = transforms.to_kernel_layout(r.T_x)
         xc, xs = ops.quant("mxfp4", Xb, bank)
         out = ops.gemm_mxfp4(xc, xs, r.codes, r.scales, out_dtype=torch.float32)
         err[mode] = float(((out.double() - exact) ** 2).mean() / (exact ** 2).mean())

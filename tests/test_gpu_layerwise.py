@@ -129,10 +129,11 @@ def test_table1_orderings_on_gpu():
     W, Xc, Xe = gen_linear_layer(2048, 512, 2048, 1024, seed=33, n_outlier=20)
     X = _dev_bf16(f64_to_bf16_bits(Xe))
     Wd = _dev_bf16(f64_to_bf16_bits(W))
+    Xcd = _dev_bf16(f64_to_bf16_bits(Xc))
     res = {}
     for fmt in ("mxfp4", "nvfp4", "int4"):
         G = 16 if fmt == "nvfp4" else 32
-        banks = layerwise.transform_pairs(torch.from_numpy(W), torch.from_numpy(Xc), G, "cuda")
+        banks = layerwise.transform_pairs(Wd, Xcd, G)
         res[fmt] = {k: layerwise.layerwise_loss(fmt, X, Wd, a, b) for k, (a, b) in banks.items()}
     print(res)
     for fmt in ("mxfp4", "int4"):

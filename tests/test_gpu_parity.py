@@ -136,9 +136,11 @@ def test_empty_batch_is_noop():
 # Hadamard factor replaced by the identity).  A cyclic shift catches a
 # transposed T.
 @pytest.mark.parametrize("which", ["identity", "hadamard", "wus", "cyclic"])
-def test_special_transforms(which):
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_special_transforms(which, fmt):
     wl = CONFIGS["tiny_mxfp4"]
-    G, C = 32, wl.C
+    G = 16 if fmt == "nvfp4" else 32
+    C = wl.K // G
     if which == "identity":
         T = np.broadcast_to(np.eye(G), (C, G, G))
     elif which == "hadamard":
@@ -152,9 +154,30 @@ def test_special_transforms(which):
                 T[c, k, (k + 2 * c + 1) % G] = 1.0
     tb = f64_to_bf16_bits(np.ascontiguousarray(T))
     xb = cases.x_full("tiny_mxfp4")
-    for fmt in ("mxfp4", "int4"):
-        c, s = _run(fmt, xb, tb)
-        parity.check(fmt, xb, tb, c, s)
+    g = _g_for(xb, tb) if fmt == "nvfp4" else None
+    c, s = _run(fmt, xb, tb, g)
+    parity.check(fmt, xb, tb, c, s, g)
+
+
+@pytest.mark.parametrize("kind", ["identity", "hadamard"])
+@pytest.mark.parametrize("G", [16, 32])
+def test_fixed_banks_match_oracle(kind, G):
+    """The library's fixed banks (wush_fixed_transforms) are bit-identical to
+    the oracle's identity and normalized Sylvester Hadamard matrices, in
+    float64 and in the bf16 kernel layout; wush_f64_to_bf16 matches the
+    oracle's bf16(fp32(.)) on random values."""
+    from mxfp4_activation_amd import ops
+
+    C = 5
+    ref = np.broadcast_to(np.eye(G) if kind == "identity" else tr.hadamard(G), (C, G, G)).copy()
+    got64 = ops.fixed_transforms(kind, C, G, "cuda", f64=True).cpu().numpy()
+    got16 = ops.fixed_transforms(kind, C, G, "cuda").view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got64, ref)
+    np.testing.assert_array_equal(got16, tr.transforms_to_bf16_bits(ref))
+    rng = np.random.default_rng(G)
+    v = rng.standard_normal((3, G, G)) * np.exp2(rng.integers(-60, 60, (3, G, G)))
+    got = ops.f64_to_bf16(torch.from_numpy(v).cuda()).view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, tr.transforms_to_bf16_bits(v))
 
 
 def test_scale_boundaries_take_exact_path():
@@ -197,20 +220,7 @@ def test_extreme_magnitudes(fmt):
         parity.check(fmt, xb, tb, c, s, g)
 
 
-# ---------------------------------------------------------------- full sizes (sampled rows)
-
-
-@pytest.mark.parametrize("name", ["llama8b_mxfp4", "downproj_mxfp4", "nvfp4", "int4"])
-def test_full_size_sampled_rows(name):
-    wl = CONFIGS[name]
-    print("case", name, wl.M, wl.K, flush=True)
-    _, tb = cases.transforms(name)
-    xb = cases.x_full(name)
-    rows = cases.sample_rows(wl.M)
-    g = cases.oracle_global_scale(name) if wl.fmt == "nvfp4" else None
-    c, s, n = _run(wl.fmt, xb, tb, g, n_exact=True)
-    rep = parity.check(wl.fmt, xb[rows], tb, c[rows], s[rows], g)
-    print(name, rep, "exact groups:", n, "of", wl.M * wl.C, flush=True)
+# ---------------------------------------------------------------- long runs
 
 
 # Batches big enough that workgroups take runs of 2 or 3 tiles, with a
@@ -226,8 +236,7 @@ def test_full_size_sampled_rows(name):
 #   of 8, so the XCD remap applies; 17 x 86 = 1462 three-tile ones, which is
 #   not.
 # All of these grids exceed one resident wave of workgroups, so they take
-# the token-major order.  The oracle checks sampled rows, which include
-# every row of the last two tiles.
+# the token-major order.  Every row is checked.
 @pytest.mark.parametrize("fmt,M,K", [("mxfp4", 4100, 4096), ("int4", 4136, 8192), ("nvfp4", 4100, 4096),
                                      ("int4", 4168, 8192), ("mxfp4", 8200, 4096),
                                      ("mxfp4", 4600, 4128), ("nvfp4", 4600, 4128), ("mxfp4", 8200, 4128)])
@@ -241,44 +250,53 @@ def test_long_runs_with_ragged_tail(fmt, M, K):
     Xc = rng.laplace(0.0, 1.0, (512, K))
     T64, _ = tr.build_transforms(W, Xc, G)
     xb, tb = f64_to_bf16_bits(X), tr.transforms_to_bf16_bits(T64)
-    rows = np.union1d(cases.sample_rows(M, n_edge=16, n_rand=48), np.arange(M - 64, M))
     g = _g_for(xb, tb) if fmt == "nvfp4" else None
     c, s = _run(fmt, xb, tb, g)
-    rep = parity.check(fmt, xb[rows], tb, c[rows], s[rows], g)
-    print(fmt, M, K, rep, flush=True)
+    for lo in range(0, M, 4096):
+        rep = parity.check(fmt, xb[lo:lo + 4096], tb, c[lo:lo + 4096], s[lo:lo + 4096], g)
+        print(fmt, M, K, lo, rep, flush=True)
 
 
 # ---------------------------------------------------------------- support entry points
 
 
-@pytest.mark.parametrize("G", [16, 32])
-def test_transform_f32_error_bounds(G):
-    _, tb = cases.transforms("tiny_mxfp4", G)
-    T64, _ = cases.transforms("tiny_mxfp4", G)
-    xb = cases.x_full("tiny_mxfp4")
+@pytest.mark.parametrize("name,G", [("tiny_mxfp4", 16), ("tiny_mxfp4", 32), ("llama8b_mxfp4", 32)])
+def test_transform_f32_error_bounds(name, G):
+    """The unquantized transform (wush_transform_f32) on the tiny workload and
+    on the whole 4096 x 4096 headline tensor.
+
+    * Against the oracle on the same bf16 inputs (the pages' 16-bit T): every
+      value within the accumulation bound the scale guard assumes, hence
+      within 2e-3 of its group's AbsMax (the benchmark spec's tolerance, asserted).
+    * Against the unrounded float64 T: the extra error is the bf16 storage of
+      T, at most bf16's unit roundoff 2^-8 per entry (plus 2^-23 from the
+      fp32 step) times sum_j |T64_kj x_j|; asserted, and the group-relative
+      deviation is printed (it runs to about 4e-3, so 2e-3 does not hold
+      against the float64 T and is not claimed there)."""
     from mxfp4_activation_amd import ops
 
+    T64, tb = cases.transforms(name, G)
+    xb = cases.x_full(name)
+    M, K = xb.shape
     Y = ops.transform_f32(_dev_bf16(xb), _dev_bf16(tb)).cpu().numpy()
-    y_ref, A = quant.transform_ref(xb, tb, return_abs=True)
-    # the accumulation bound assumed by the scale fix-up
-    bound = (2.0 ** -17) * A + (2.0 ** -21) * np.abs(y_ref) + 2.0 ** -120
-    assert np.all(np.abs(Y.astype(np.float64) - y_ref) <= bound)
-    # Pre-quantization tolerance: within 2e-3 of the group AbsMax of the
-    # oracle's values for the same bf16 T.
-    M, K = y_ref.shape
-    err = np.abs(Y - y_ref).reshape(M, K // G, G).max(axis=2)
-    amax = np.abs(y_ref).reshape(M, K // G, G).max(axis=2)
-    assert np.all(err <= 2e-3 * amax)
-    # Against the unrounded float64 T, the extra error is bf16 storage of T.
-    # Each entry moves by at most bf16's unit roundoff 2^-8 relative, plus
-    # 2^-24 from the fp32 step.  So |y - y64| <= (2^-8 + 2^-23) *
-    # sum_j |T64_kj x_j| plus the bound above.
-    y64 = quant.transform_f64(xb, T64)
-    X = codecs.bf16_bits_to_f32(xb).astype(np.float64).reshape(M, K // G, G)
-    A64 = np.einsum("mcj,ckj->mck", np.abs(X), np.abs(T64)).reshape(M, K)
-    assert np.all(np.abs(Y - y64) <= (2.0 ** -8 + 2.0 ** -23) * A64 + bound)
-    rel = (np.abs(Y - y64).reshape(M, K // G, G).max(axis=2) / np.abs(y64).reshape(M, K // G, G).max(axis=2))
-    print("G=%d relative error vs float64 T: median %.2e, max %.2e" % (G, np.median(rel), rel.max()))
+    for lo in range(0, M, 4096):
+        x, yg = xb[lo:lo + 4096], Y[lo:lo + 4096].astype(np.float64)
+        m = x.shape[0]
+        y_ref, A = quant.transform_ref(x, tb, return_abs=True)
+        bound = (2.0 ** -17) * A + (2.0 ** -21) * np.abs(y_ref) + 2.0 ** -120
+        assert np.all(np.abs(yg - y_ref) <= bound)
+        err = np.abs(yg - y_ref).reshape(m, K // G, G).max(axis=2)
+        amax = np.abs(y_ref).reshape(m, K // G, G).max(axis=2).astype(np.float64)
+        assert np.all(err <= 2e-3 * amax)
+        y64 = quant.transform_f64(x, T64)
+        Xc = codecs.bf16_bits_to_f32(x).astype(np.float64).reshape(m, K // G, G).transpose(1, 0, 2)
+        A64 = np.matmul(np.abs(Xc), np.abs(T64).transpose(0, 2, 1)).transpose(1, 0, 2).reshape(m, K)
+        assert np.all(np.abs(yg - y64) <= (2.0 ** -8 + 2.0 ** -23) * A64 + bound)
+        g64 = np.abs(y64).reshape(m, K // G, G).max(axis=2)
+        rel = np.abs(yg - y64).reshape(m, K // G, G).max(axis=2) / np.where(g64 > 0, g64, 1.0)
+        print("%s G=%d rows %d..: vs same-bf16-T oracle max %.2e of the group AbsMax; vs float64 T median %.2e, "
+              "p99.9 %.2e, max %.2e" % (name, G, lo, (err / np.where(amax > 0, amax, 1.0)).max(), np.median(rel),
+                                         np.quantile(rel, 0.999), rel.max()), flush=True)
 
 
 @pytest.mark.parametrize("G,rows,blocks", [
@@ -296,14 +314,14 @@ def test_absmax_and_global_scale(G, rows, blocks):
     if rows is not None:
         xb = np.ascontiguousarray(xb[:rows, : blocks * G])
         tb = np.ascontiguousarray(tb[:blocks])
-    y, A = quant.transform_ref(xb, tb, return_abs=True)
+    y = quant.transform_ref(xb, tb)
     X, T = _dev_bf16(xb), _dev_bf16(tb)
-    amax = float(ops.transformed_absmax(X, T).item())
-    ref = float(quant.tensor_amax_ref(y))
-    assert abs(amax - ref) <= (2.0 ** -17) * A.max() + (2.0 ** -21) * ref
+    amax = np.float32(ops.absmax_transformed(X, T).item())
+    ref = quant.tensor_amax_ref(y)
+    assert amax.view(np.uint32) == ref.view(np.uint32), (amax, ref)  # bit-exact
     if G == 16:
-        g = float(ops.nvfp4_global_scale(X, T).item())
-        assert g == float(np.float32(np.float32(amax) / np.float32(2688.0)))
+        g = np.float32(ops.nvfp4_global_scale(X, T).item())
+        assert g.view(np.uint32) == quant.nvfp4_global_scale(ref).view(np.uint32)
 
 
 @pytest.mark.parametrize("planted", [8199, 4111])
@@ -320,10 +338,10 @@ def test_absmax_three_tile_runs(planted):
     X = rng.standard_normal((M, K))  # light tails: no other row comes near the planted one
     X[planted] *= 1000.0
     xb = f64_to_bf16_bits(X)
-    y, A = quant.transform_ref(xb[planted:planted + 1], tb, return_abs=True)
-    ref = float(np.abs(y).max())
-    amax = float(ops.transformed_absmax(_dev_bf16(xb), _dev_bf16(tb)).item())
-    assert abs(amax - ref) <= (2.0 ** -17) * A.max() + (2.0 ** -21) * ref, (amax, ref)
+    y = quant.transform_ref(xb[planted:planted + 1], tb)
+    ref = quant.tensor_amax_ref(y)
+    amax = np.float32(ops.absmax_transformed(_dev_bf16(xb), _dev_bf16(tb)).item())
+    assert amax.view(np.uint32) == ref.view(np.uint32), (amax, ref)
 
 
 def test_absmax_empty_is_zero():
@@ -332,50 +350,143 @@ def test_absmax_empty_is_zero():
     _, tb = cases.transforms("tiny_mxfp4", 16)
     X = torch.empty((0, tb.shape[0] * 16), dtype=torch.bfloat16, device="cuda")
     out = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
-    ops.transformed_absmax(X, _dev_bf16(tb), out=out)
+    ops.absmax_transformed(X, _dev_bf16(tb), out=out)
     assert float(out.item()) == 0.0
 
 
 def test_global_scale_full_nvfp4_workload():
-    """The AbsMax pre-pass over the whole 16384 x 4096 NVFP4 tensor against
-    the oracle's.  Bound: the fp32 accumulation error of one output,
-    2^-17 * sum_j |T_kj x_j| (bounded by the largest row L1 norm of |T|
-    times max |x|), plus the final rounding."""
+    """The AbsMax pre-pass over the whole 16384 x 4096 NVFP4 tensor equals the
+    oracle's exact maximum bit for bit, so the device g equals the oracle's g."""
     from mxfp4_activation_amd import ops
 
     _, tb = cases.transforms("nvfp4")
     xb = cases.x_full("nvfp4")
     X, T = _dev_bf16(xb), _dev_bf16(tb)
-    amax = float(ops.transformed_absmax(X, T).item())
-    g = float(ops.nvfp4_global_scale(X, T).item())
-    g_ref = float(cases.oracle_global_scale("nvfp4"))
-    ref = g_ref * 2688.0
-    t_l1 = np.abs(codecs.bf16_bits_to_f32(tb).astype(np.float64)).sum(axis=2).max()
-    x_max = np.abs(codecs.bf16_bits_to_f32(xb)).max()
-    assert abs(amax - ref) <= (2.0 ** -17) * t_l1 * x_max + (2.0 ** -20) * ref, (amax, ref)
-    assert g == float(np.float32(np.float32(amax) / np.float32(2688.0)))
+    amax = np.float32(ops.absmax_transformed(X, T).item())
+    g = np.float32(ops.nvfp4_global_scale(X, T).item())
+    g_ref = cases.oracle_global_scale("nvfp4")
+    ref = np.float32(cases.oracle_tensor_amax("nvfp4"))
     print("AbsMax %.9g, oracle %.9g, g %.9g, oracle g %.9g" % (amax, ref, g, g_ref))
+    assert amax.view(np.uint32) == ref.view(np.uint32)
+    assert g.view(np.uint32) == g_ref.view(np.uint32)
 
 
-def test_deterministic_and_in_bounds():
-    """Two runs give identical bytes.  Canary bytes around the outputs stay
-    untouched."""
+@pytest.mark.parametrize("G", [16, 32])
+def test_absmax_near_ties(G):
+    """Tokens whose transformed maxima differ by a few ulps or less, spread over
+    workgroups: the pass must return the exact maximum, not a matrix-core
+    value that rounds past it.  T = I + eps R keeps every output within
+    about 2^-18 of its identity value, so many candidates tie within the
+    accumulation bound."""
     from mxfp4_activation_amd import ops
 
-    _, tb = cases.transforms("tiny_mxfp4")
-    xb = cases.x_full("tiny_mxfp4")
-    M, K = xb.shape
-    X, T = _dev_bf16(xb), _dev_bf16(tb)
+    rng = np.random.default_rng(70 + G)
+    M, C = 4100, 16
+    K = C * G
+    X = rng.uniform(-1, 1, (M, K))
+    top = 1.75 * (1 + rng.integers(-3, 4, 40) * 2.0 ** -7)  # bf16 values within a few ulps of each other
+    rows = rng.choice(M, 40, replace=False)
+    X[rows, rng.integers(0, K, 40)] = top
+    T = np.broadcast_to(np.eye(G), (C, G, G)) + rng.standard_normal((C, G, G)) * 2.0 ** -18
+    xb, tb = f64_to_bf16_bits(X), f64_to_bf16_bits(T)
+    ref = quant.tensor_amax_ref(quant.transform_ref(xb, tb))
+    amax = np.float32(ops.absmax_transformed(_dev_bf16(xb), _dev_bf16(tb)).item())
+    assert amax.view(np.uint32) == ref.view(np.uint32), (amax, ref)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_zero_rows_need_no_recompute(fmt):
+    """All-zero tokens (padding) take no exact recompute: an all-zero tensor
+    counts none, and a tensor whose first half is zero counts exactly what
+    its second half counts alone.  Outputs are zero codes and the minimum
+    scale code, and the rest matches the oracle."""
+    G = 16 if fmt == "nvfp4" else 32
+    M, C = 512, 16
+    K = C * G
+    rng = np.random.default_rng(17)
+    T = rng.standard_normal((C, G, G)) * 0.25
+    tb = f64_to_bf16_bits(T)
+    X = rng.standard_t(3, (M, K))
+    X[: M // 2] = 0.0
+    X[: M // 2: 7] = -0.0
+    xb = f64_to_bf16_bits(X)
+    g = np.float32(2.0 ** -4)
+    c, s, n_zero = _run(fmt, np.zeros((M // 2, K), dtype=np.uint16), tb, g, n_exact=True)
+    assert n_zero == 0
+    assert not c.any() and not s.any()
+    c, s, n_mixed = _run(fmt, xb, tb, g, n_exact=True)
+    _, _, n_half = _run(fmt, np.ascontiguousarray(xb[M // 2:]), tb, g, n_exact=True)
+    assert n_mixed == n_half, (n_mixed, n_half)
+    parity.check(fmt, xb, tb, c, s, g)
+
+
+def test_planted_e4m3_boundaries():
+    """NVFP4 groups whose maximum sits on or right next to an E4M3 rounding
+    midpoint of fp32(fp32(amax / 6) / g), across the normal and subnormal
+    E4M3 range, with a static g.  T = I + eps R: with eps = 2^-19 the
+    perturbation is below the accumulation bound, so the guard must send the
+    group to the exact path; with eps = 2^-10 it moves the maximum off the
+    midpoint by about 2^-9 relative, on either side."""
+    G, C, M = 16, 16, 512
+    K = C * G
+    g = 2.0 ** -6
+    rng = np.random.default_rng(23)
+    # E4M3 values (codes 1..126) and the midpoints between neighbours
+    e4 = np.array([(m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+                   for e in range(16) for m in range(8)])[1:127]
+    mids = (e4[:-1] + e4[1:]) / 2
+    X = rng.uniform(-0.3, 0.3, (M, K))
+    targets = rng.choice(mids, (M, C)) * 6.0 * g
+    X = X * (targets.repeat(G, axis=1) / 0.3)  # group values below the planted maximum
+    pos = rng.integers(0, G, (M, C))
+    sign = rng.choice([-1.0, 1.0], (M, C))
+    for c in range(C):
+        X[np.arange(M), c * G + pos[:, c]] = sign[:, c] * targets[:, c]
+    xb = f64_to_bf16_bits(X)
+    eps = np.where(np.arange(C) < C // 2, 2.0 ** -19, 2.0 ** -10)[:, None, None]
+    T = np.broadcast_to(np.eye(G), (C, G, G)) + eps * rng.standard_normal((C, G, G))
+    tb = f64_to_bf16_bits(T)
+    c, s, n = _run("nvfp4", xb, tb, np.float32(g), n_exact=True)
+    rep = parity.check("nvfp4", xb, tb, c, s, np.float32(g))
+    print("planted E4M3 midpoints: %d exact groups of %d; %s" % (n, M * C, rep))
+    assert n > 0
+
+
+def test_guard_bytes_every_store_path():
+    """Canary bytes before and after the code and scale buffers stay
+    untouched, and two runs give identical bytes, on every store path:
+    whole-tile runs of 1, 2 and 3 tiles, ragged token and channel edges, the
+    G = 16 half-panel store (K/2 not a multiple of 16), and each format's
+    scale width.  Stops at the first failure."""
+    from mxfp4_activation_amd import ops
+
+    shapes = [("mxfp4", 128, 256), ("mxfp4", 4096, 4096), ("mxfp4", 8200, 4096), ("mxfp4", 100, 96),
+              ("mxfp4", 33, 4096 + 32), ("nvfp4", 64, 48), ("nvfp4", 40, 272), ("nvfp4", 4100, 4096),
+              ("nvfp4", 256, 512), ("int4", 256, 512), ("int4", 100, 96), ("int4", 4136, 8192)]
     pad = 4096
-    cbuf = torch.full((pad + M * K // 2 + pad,), 0xA5, dtype=torch.uint8, device="cuda")
-    sbuf = torch.full((pad + M * K // 32 + pad,), 0x5A, dtype=torch.uint8, device="cuda")
-    codes = cbuf[pad:pad + M * K // 2].view(M, K // 2)
-    scales = sbuf[pad:pad + M * K // 32].view(M, K // 32)
-    ops.quant("mxfp4", X, T, codes=codes, scales=scales)
-    first = (codes.clone(), scales.clone())
-    ops.quant("mxfp4", X, T, codes=codes, scales=scales)
-    torch.cuda.synchronize()
-    assert torch.equal(first[0], codes) and torch.equal(first[1], scales)
-    cb, sb = cbuf.cpu().numpy(), sbuf.cpu().numpy()
-    assert np.all(cb[:pad] == 0xA5) and np.all(cb[-pad:] == 0xA5)
-    assert np.all(sb[:pad] == 0x5A) and np.all(sb[-pad:] == 0x5A)
+    for fmt, M, K in shapes:
+        print("case", fmt, M, K, flush=True)
+        G = 16 if fmt == "nvfp4" else 32
+        rng = np.random.default_rng(M + K)
+        xb = f64_to_bf16_bits(rng.standard_t(3, (M, K)))
+        tb = f64_to_bf16_bits(rng.standard_normal((K // G, G, G)) * 0.2)
+        X, T = _dev_bf16(xb), _dev_bf16(tb)
+        sbytes = 2 if fmt == "int4" else 1
+        cbuf = torch.full((pad + M * K // 2 + pad,), 0xA5, dtype=torch.uint8, device="cuda")
+        sbuf = torch.full((pad + M * (K // G) * sbytes + pad,), 0x5A, dtype=torch.uint8, device="cuda")
+        codes = cbuf[pad:pad + M * K // 2].view(M, K // 2)
+        scales = sbuf[pad:pad + M * (K // G) * sbytes]
+        scales = (scales.view(torch.float16) if fmt == "int4" else scales).view(M, K // G)
+        gs = torch.tensor([np.float32(2.0 ** -3)], dtype=torch.float32, device="cuda")
+        ops.quant(fmt, X, T, global_scale=gs, codes=codes, scales=scales)
+        first = (codes.clone(), scales.clone())
+        ops.quant(fmt, X, T, global_scale=gs, codes=codes, scales=scales)
+        torch.cuda.synchronize()
+        assert torch.equal(first[0], codes) and torch.equal(first[1], scales), (fmt, M, K)
+        cb, sb = cbuf.cpu().numpy(), sbuf.cpu().numpy()
+        assert np.all(cb[:pad] == 0xA5) and np.all(cb[-pad:] == 0xA5), (fmt, M, K, "codes")
+        assert np.all(sb[:pad] == 0x5A) and np.all(sb[-pad:] == 0x5A), (fmt, M, K, "scales")
+        if M * K <= 1 << 20:
+            s_np = scales.cpu().numpy()
+            parity.check(fmt, xb, tb, codes.cpu().numpy(), s_np.view(np.uint16) if fmt == "int4" else s_np,
+                         np.float32(2.0 ** -3))
