@@ -42,15 +42,17 @@
  * sum_j T[c][i][j] * x_j.  The kernels use fp32 matrix-core accumulation,
  * which can differ from the exact sum by an error bounded by the sum of
  * |T x| terms.  Any group whose scale decision falls within that bound of
- * a rounding boundary is recomputed: the G products (each exact in
- * float64) are summed in float64 and rounded once to fp32.  That sum is
- * exact when the products span at most 32 binary octaves; beyond that its
- * error stays below 2^-47 of the sum of |T x| terms, so the recomputed y
- * can differ from the exactly rounded one only if the exact sum lies that
- * close to an fp32 rounding midpoint.  With that proviso every scale equals
- * the one computed from the exactly rounded y.  An element code may still
- * differ by one level where the scaled value sits within the accumulation
- * bound of a rounding midpoint.
+ * a rounding boundary gets its exact AbsMax: each output that can hold the
+ * maximum (within twice the bound of the largest matrix-core value) is
+ * recomputed from its G products (each exact in float64), summed in
+ * float64 and rounded once to fp32.  That sum is exact when the products
+ * span at most 32 binary octaves; beyond that its error stays below 2^-47
+ * of the sum of |T x| terms, so the recomputed y can differ from the
+ * exactly rounded one only if the exact sum lies that close to an fp32
+ * rounding midpoint.  With that proviso every scale equals the one
+ * computed from the exactly rounded y.  An element code may still differ
+ * by one level where the scaled value sits within the accumulation bound
+ * of a rounding midpoint.
  */
 #ifndef WUSH_H_
 #define WUSH_H_
@@ -109,7 +111,8 @@ wush_status wush_quant_int4(const void* X, const void* T, int64_t M, int64_t K,
  * fmt: 0 = MXFP4, 1 = NVFP4, 2 = INT4.
  * global_scale: used only for NVFP4.
  * n_exact: if non-null, a device uint32 to which the kernel atomically adds
- * the number of groups it recomputed in float64.  The caller zeroes it. */
+ * the number of token panels (32 channels of one token: one group, or two
+ * for NVFP4) with a group that took the exact step.  The caller zeroes it. */
 wush_status wush_quant(int fmt, const void* X, const void* T, int64_t M, int64_t K,
                        const float* global_scale, void* codes, void* scales,
                        uint32_t* n_exact, hipStream_t stream);

@@ -230,16 +230,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // owns output row permuted_row(i): its T fragment (the MFMA A operand) is
 // exactly its half-row of T, and it forms the half-h partial sum; lane
 // l ^ 32 holds the other half.  Token n's channels of the panel come from
-// the lanes that hold them (readlane), or, with XLDS, from the staged tile
-// (LDS address `xtok`, its row at this panel; the same 16 bytes for every
-// lane of a half, a broadcast read).  XLDS costs 8 VGPRs in this path and
-// saves about 40 instructions per call; it is used where the register
-// budget allows it.  The fragment is copied through an empty asm
-// statement, so the compiler cannot hoist this rare path's float64
-// conversions of T out of the hot loop into registers that stay live.
-template <bool XLDS>
-__device__ __forceinline__ void exact_panel(uint32_t xtok, const XTile& x, const Frag& f, f32x16& acc, float* lds,
-                                            int n, int lane) {
+// the staged tile (LDS address `xtok`, its row at this panel; the same 16
+// bytes for every lane of a half, a broadcast read).  The fragment is
+// copied through an empty asm statement, so the compiler cannot hoist this
+// rare path's float64 conversions of T out of the hot loop into registers
+// that stay live.
+__device__ __forceinline__ void exact_panel(uint32_t xtok, const Frag& f, f32x16& acc, float* lds, int n, int lane) {
   // Addresses below derive from an opaque copy of the lane id, so the
   // compiler keeps their arithmetic inside this rarely taken path.
   int lds_off = 0;
@@ -249,26 +245,16 @@ __device__ __forceinline__ void exact_panel(uint32_t xtok, const XTile& x, const
   const int row = permuted_row(i);
   u32x4 tk[2] = {f.t0, f.t1};
   asm volatile("" : "+v"(tk[0]), "+v"(tk[1]));
-  u32x4 bk[2] = {x.b0, x.b1};
-  if (XLDS) {
-    lds_cu8* xp = (lds_cu8*)(uintptr_t)(xtok + 16 * h);
-    bk[0] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(xp);
-    bk[1] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(xp + 32);
-  }
+  lds_cu8* xp = (lds_cu8*)(uintptr_t)(xtok + 16 * h);
+  const u32x4 bk[2] = {*reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(xp),
+                       *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(xp + 32)};
   double s = 0.0;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t xw;
-      if (XLDS) {
-        xw = bk[kk][w];
-      } else {
-        uint32_t x0 = __builtin_amdgcn_readlane(bk[kk][w], n);
-        uint32_t x1 = __builtin_amdgcn_readlane(bk[kk][w], n + 32);
-        xw = h ? x1 : x0;
-      }
-      uint32_t tw = tk[kk][w];
+      const uint32_t xw = bk[kk][w];
+      const uint32_t tw = tk[kk][w];
       s = __builtin_fma((double)bf16_lo(tw), (double)bf16_lo(xw), s);
       s = __builtin_fma((double)bf16_hi(tw), (double)bf16_hi(xw), s);
     }
@@ -285,6 +271,41 @@ __device__ __forceinline__ void exact_panel(uint32_t xtok, const XTile& x, const
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// A-operand row that holds output k: the inverse of permuted_row.
+__device__ __forceinline__ int row_of_output(int k) {
+  return (k & 3) | (((k >> 4) & 1) << 2) | (((k >> 2) & 3) << 3);
+}
+
+// Exact value of output k of this lane's token, rounded once to fp32.
+// Lane (n, h) multiplies its own 16 channels of the token (its B operand:
+// k-slice 0 at LDS address xo, k-slice 1 at xo + 32) by the matching 16
+// entries of T row k, which A-operand lane (row_of_output(k), h) holds;
+// ds_bpermute fetches them.  Each product of two bf16 values is exact in
+// float64; the two halves are summed with sum_halves, so lanes (n, 0) and
+// (n, 1) get the same value when both ask for the same k.  Lanes may ask
+// for different outputs (one per token), which makes the pass lane-parallel.
+// The channels are read one word pair at a time through an opaque address:
+// held in registers across the caller's loop they would cost 8 VGPRs, and
+// their float64 conversions, hoisted, 32.
+__device__ __forceinline__ float exact_output(const Frag& f, uint32_t xo, int k, int lane) {
+  asm volatile("" : "+v"(xo));
+  typedef const __attribute__((address_space(3))) uint32_t lds_u32;
+  const int src = (row_of_output(k) + (lane & 32)) << 2;  // byte address of the source lane
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x0 = *reinterpret_cast<lds_u32*>((lds_cu8*)(uintptr_t)(xo + 4 * w));
+    const uint32_t x1 = *reinterpret_cast<lds_u32*>((lds_cu8*)(uintptr_t)(xo + 32 + 4 * w));
+    const uint32_t t0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)f.t0[w]);
+    const uint32_t t1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)f.t1[w]);
+    s = __builtin_fma((double)bf16_lo(t0), (double)bf16_lo(x0), s);
+    s = __builtin_fma((double)bf16_hi(t0), (double)bf16_hi(x0), s);
+    s = __builtin_fma((double)bf16_lo(t1), (double)bf16_lo(x1), s);
+    s = __builtin_fma((double)bf16_hi(t1), (double)bf16_hi(x1), s);
+  }
+  return (float)sum_halves(s);
 }
 
 // 16 values -> 16 E2M1 codes in two words, value r in nibble r.  `scale` is
@@ -380,11 +401,11 @@ __device__ __forceinline__ void wg_coords(int n_pg, int n_tg, int token_major, i
 // token n) and `bound`, an upper bound on sum_j |T_kj x_j| over the lane's
 // group.  Output: this lane's 16 codes (two words) and its scale bits.
 // Groups whose scale decision falls within the accumulation error bound of
-// a boundary are recomputed exactly first.
-template <int FMT, bool XLDS>
+// a boundary first get their exact AbsMax, from the few outputs that can
+// hold it.
+template <int FMT>
 __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float bound_scale, const Frag& f,
-                                                const XTile& x, uint32_t tile, int tile_stride, float g, float* lds,
-                                                int lane,
+                                                uint32_t tile, int tile_stride, float g, int lane,
                                                 uint32_t& scale_bits, uint32_t& n_exact) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   float amax = max_abs16(acc);
@@ -403,6 +424,11 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
   }
   uint64_t pending = __ballot(unsure);
   if (pending) {
+    // The lane's own 16 channels of the token sit in the staged tile at
+    // `xo` (k-slice 0) and xo + 32 (k-slice 1): its B operand.
+    typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+    const int h = lane >> 5;
+    const uint32_t xo = tile + (uint32_t)((lane & 31) * tile_stride + 16 * h);
     // MXFP4: a token whose channels in this panel are all zero (either
     // sign) has y = 0 exactly, and the matrix cores return exactly zero for
     // it, so it needs no recompute.  Zero-padded rows would otherwise all
@@ -410,25 +436,52 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
     // several E8M0 codes.  (The INT4 and NVFP4 decisions are already
     // settled for them: fp16 and E4M3 both round that interval to 0.)
     if (FMT == kMXFP4) {
-      typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
-      const uint32_t xo = tile + (uint32_t)((lane & 31) * tile_stride + 16 * (lane >> 5));
       const u32x4 q0 = *reinterpret_cast<lds_u32x4*>((lds_cu8*)(uintptr_t)xo);
       const u32x4 q1 = *reinterpret_cast<lds_u32x4*>((lds_cu8*)(uintptr_t)(xo + 32));
       const uint32_t any = (q0[0] | q0[1] | q0[2] | q0[3] | q1[0] | q1[1] | q1[2] | q1[3]) & 0x7FFF7FFFu;
       const uint64_t zl = __ballot(any == 0u);
       const uint64_t zt = zl & (zl >> 32) & 0xFFFFFFFFull;  // both halves of token n zero
       pending &= ~(zt | (zt << 32));
+      unsure = unsure && !((zt >> (lane & 31)) & 1u);
     }
-    while (pending) {
-      int ln = __builtin_ctzll(pending) & 31;
-      exact_panel<XLDS>(tile + ln * tile_stride, x, f, acc, lds, ln, lane);
-      pending &= ~((1ull << ln) | (1ull << (ln + 32)));
-      ++n_exact;  // wave-uniform count
+    n_exact += (uint32_t)__builtin_popcountll((pending | (pending >> 32)) & 0xFFFFFFFFull);  // wave-uniform
+    // Candidates: every output's exact value is within d of its
+    // matrix-core value, so the exact maximum is at least amax - d and the
+    // output that holds it has |y^_k| >= amax - 2d.  The cut is taken at
+    // amax - 2.25d: d >= 2^-21 amax, so the extra quarter covers the
+    // rounding of the subtraction.  Only the candidates are recomputed, one
+    // output per token per pass, all tokens of the tile at once; the
+    // maximum over a group's candidates is its exact AbsMax.  The codes
+    // keep the matrix-core values: with the exact scale they can differ
+    // from the exactly rounded ones only within the accumulation bound of a
+    // rounding midpoint.
+    uint32_t cand = 0u;
+    if (unsure) {
+      const float lo = amax - 2.25f * d;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cand |= (fabsf(acc[r]) >= lo ? 1u : 0u) << r;
     }
-    amax = max_abs16(acc);
-    if (G == 32) amax = max_halves(amax);
-    // Decide again at the new amax (the same value for the groups that were
-    // not recomputed).
+    // Both lanes of a token see its 32 candidate bits, output k at bit k:
+    // in both halves the swap's first result is the value of lane (n, 0),
+    // the second that of lane (n, 1).
+    // The wave takes as many passes as its token with the most candidates:
+    // almost always one, at most 32 (32 near-equal outputs).  A pass costs
+    // about what recomputing one token's whole panel does.
+    const auto sw = __builtin_amdgcn_permlane32_swap(cand, cand, false, false);
+    uint32_t m = sw[0] | (sw[1] << 16);
+    if (__ballot(m != 0u)) {
+      float ex = 0.0f;
+      do {
+        const int kk = m ? __builtin_ctz(m) : 0;
+        const float yk = exact_output(f, xo, kk, lane);
+        if (m && (G == 32 || (kk >> 4) == h)) ex = fmaxf(ex, fabsf(yk));
+        m &= m - 1u;
+      } while (__ballot(m != 0u));
+      // An unsure group has a candidate (its largest |y^_k| is one); a
+      // settled group keeps its amax.
+      if (unsure) amax = ex;
+    }
+    // Decide again at the new amax (the same value for the settled groups).
     if (FMT == kINT4) sdec = f16_bits(amax / 7.0f);
     if (FMT == kNVFP4 && g > 0.0f) sdec = e4m3_code((amax / 6.0f) / g);
   }
@@ -545,9 +598,9 @@ struct QuantLds {
 // L1 norms (of a token pair, see below); bscale is max|T| * 2^-17.  INT4 and NVFP4 scales have much denser
 // boundaries, so they use the per-output bound max_k sum_j |T_kj x_j| from
 // an |T| x |x| MFMA, with bscale = 2^-17.
-template <int FMT, bool XLDS>
-__device__ __forceinline__ void panel_step(uint8_t* row, float* ybuf, const Frag& f, const u32x4& ones, float bscale,
-                                           float g, int wave, int lane, uint32_t& n_exact) {
+template <int FMT>
+__device__ __forceinline__ void panel_step(uint8_t* row, const Frag& f, const u32x4& ones, float bscale, float g,
+                                           int wave, int lane, uint32_t& n_exact) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   const int h = lane >> 5;
   const u32x4 mask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
@@ -582,7 +635,7 @@ __device__ __forceinline__ void panel_step(uint8_t* row, float* ybuf, const Frag
   // LDS address of row 0 of the staged tile at this wave's panel: the exact
   // recompute reads a token's channels there.
   const uint32_t tile = (uint32_t)(uintptr_t)(lds_cu8*)(row - (lane & 31) * kXRow + wave * 64);
-  const u32x2 w = quantize_panel<FMT, XLDS>(acc, bound, bscale, f, x, tile, kXRow, g, ybuf, lane, sbits, n_exact);
+  const u32x2 w = quantize_panel<FMT>(acc, bound, bscale, f, tile, kXRow, g, lane, sbits, n_exact);
   // Every lane of the wave has read its operands before any lane writes:
   // the reads above feed the MFMAs whose results the writes depend on.
   *reinterpret_cast<u32x2*>(row + wave * 64 + 8 * h) = w;
@@ -682,11 +735,10 @@ __device__ __forceinline__ void amax_run(const QuantArgs& a, QuantLds<TPW>& L, F
       const uint64_t c = __ballot(cand);
       const uint32_t tokens = (uint32_t)c | (uint32_t)(c >> 32);  // token n: lane n or n + 32
       const uint32_t tile = (uint32_t)(uintptr_t)(lds_cu8*)(L.xs[u] + wave * 64);
-      const XTile none = {b0, b1};
       uint32_t pend = tokens;
       while (pend) {
         const int n = __builtin_ctz(pend);
-        exact_panel<true>(tile + n * kXRow, none, f, acc, L.y[wave], n, lane);
+        exact_panel(tile + n * kXRow, f, acc, L.y[wave], n, lane);
         pend &= pend - 1;
       }
       if ((tokens >> (lane & 31)) & 1u) m = fmaxf(m, max_abs16(acc));
@@ -779,12 +831,7 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       if (!FULL && u >= n_tiles) break;
-      // The staged-tile read in the exact path needs registers that only
-      // the three-tile kernels have to spare (their LDS allows three
-      // workgroups per CU, so they are held to 85 VGPRs, not 64); INT4
-      // takes that path often (see quantize_panel).
-      panel_step<FMT, FMT == kINT4 && TPW == 3>(row + u * (32 * kXRow), L.y[wave], f, ones, bscale, g, wave, lane,
-                                                 n_exact);
+      panel_step<FMT>(row + u * (32 * kXRow), f, ones, bscale, g, wave, lane, n_exact);
     }
   }
   __syncthreads();
