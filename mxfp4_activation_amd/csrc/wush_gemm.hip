@@ -24,9 +24,9 @@
 //
 // Operands go from global memory straight into LDS (global_load_lds, 16 B
 // per lane, whole 128-byte rows), through a ring of step stages (4 at
-// TM = 2, 8 at TM = 1), 2 or 4 steps ahead of the MFMAs.  No staging registers and no LDS write
-// instructions are involved; each wave waits for its own loads with vmcnt
-// and one barrier per step publishes them.
+// TM = 2, 8 at TM = 1), 2 or 4 steps ahead of the MFMAs.  No staging
+// registers and no LDS write instructions are involved; each wave waits for
+// its own loads with vmcnt and one barrier per step publishes them.
 //
 // LDS layout of a stage (BT = 64 TM rows): A codes [BT rows][128 B], B
 // codes [BT][128 B], A scales [BT][8 B], B scales [BT][8 B].  A load instruction writes 1 KB
@@ -38,14 +38,17 @@
 // word is shifted right by 8 h so that op_sel 2 (s % 2) picks it for both
 // lane halves.
 //
-// Fragment reads are inline-asm ds_read blocks that wait for their own
-// results: plain LDS loads after a global_load_lds make the compiler wait
-// for every outstanding global load, which would drain the ring.  Group 1
-// runs its MFMAs before its reads in every step (on registers read in the
-// step before), so that on each SIMD one wave reads LDS while the other
-// keeps the matrix unit busy.
+// The global-to-LDS copies are issued from inline asm.  Issued through the
+// compiler builtin, they make the compiler wait for every outstanding copy
+// before any later LDS read (it cannot tell the ring stages apart), which
+// drains the ring.  Issued from asm, they are invisible to that analysis;
+// the per-step vmcnt waits below order them, and the fragment reads are
+// plain LDS loads that the compiler schedules.  Each step is software
+// pipelined within the wave: the fragments of step ks + 1 are read while
+// the MFMAs of step ks run, from a second set of registers.
 //
-// The result goes through LDS once more, so that C is written with 16-byte
+// At the end each K group writes its partial tile into its own fp32 region
+// of LDS; the store pass adds the two and writes C with 16-byte
 // row-contiguous stores.
 
 #include <hip/hip_runtime.h>
@@ -82,9 +85,8 @@ struct Geo {
   static constexpr int kLoadsPerStep = 2 * TM + 1;          // load instructions per wave per step
   static constexpr int kCRow = BT + 4;                      // padded fp32 row of the output tile
   static_assert(kStages * kStageB == kLdsB, "stages must fill the ring");
-  static_assert(kStages >= kAhead + 1, "ring too short for the load distance");
-  static_assert(kLdsB >= 8 * TM * TM * 8 * 64 * 4, "exchange does not fit");
-  static_assert(kLdsB >= BT * kCRow * 4, "output tile does not fit");
+  static_assert(kStages >= kAhead + 2, "ring too short: the stage refilled must not be the one still being read");
+  static_assert(kLdsB >= 2 * BT * kCRow * 4, "the two partial output tiles do not fit");
 };
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
@@ -111,11 +113,22 @@ __device__ __forceinline__ void wait_barrier() {
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef const __attribute__((address_space(1))) uint8_t glb_u8;
 
-// Global-to-LDS copies of 16 and 4 bytes per lane.  Kept out of the kernel
-// template: the builtin used directly in a template body makes the host pass
-// drop the kernel's launch stub without a diagnostic.
-__device__ __forceinline__ void dma16(glb_u8* src, lds_u8* dst) { __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0); }
-__device__ __forceinline__ void dma4(glb_u8* src, lds_u8* dst) { __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0); }
+// Global-to-LDS copies of 16 and 4 bytes per lane to LDS address `dst`
+// (wave-uniform; lane l writes at dst + l * size).  The copy takes its LDS
+// base from M0.  M0 is declared clobbered; the compiler reserves M0 and
+// warns that it does not preserve it across the statement, which is safe
+// here because nothing else in these kernels uses M0 (the only M0 writes in
+// their code are these).  The statements have no outputs, so no register
+// can be overwritten by a copy in flight.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(glb_u8* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(glb_u8* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(dst) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 template <int TM, bool BF16_OUT>
 __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
@@ -162,15 +175,16 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   const int s_dst = (s_is_a ? Gm::kOffSA : Gm::kOffSB) + 128 * TM * (wave & 3);
 
   // Step ks lives in ring stage ks % kStages.
+  const uint32_t wave_u = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int ks) {
     const int64_t kc = ks;
-    lds_u8* st = Ls + (ks % Gm::kStages) * Gm::kStageB;
+    const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lbase + (ks % Gm::kStages) * Gm::kStageB));
 #pragma unroll
     for (int q = 0; q < TM; ++q) {
-      dma16(a_src[q] + kc * kRowB, st + 1024 * (TM * wave + q));
-      dma16(b_src[q] + kc * kRowB, st + Gm::kOffB + 1024 * (TM * wave + q));
+      dma16(a_src[q] + kc * kRowB, st + 1024 * (TM * wave_u + q));
+      dma16(b_src[q] + kc * kRowB, st + Gm::kOffB + 1024 * (TM * wave_u + q));
     }
-    if (s_lane) dma4(s_src + kc * 8, st + s_dst);
+    if (s_lane) dma4(s_src + kc * 8, st + (uint32_t)__builtin_amdgcn_readfirstlane(s_dst));
   };
 
   f32x16 acc[TM][TM];
@@ -195,66 +209,51 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
     u32x4 a[2][TM], b[2][TM];  // [sub-step][tile]
     uint32_t sa[TM], sb[TM];
   };
+  typedef const __attribute__((address_space(3))) u32x4 lds_v4;
+  typedef const __attribute__((address_space(3))) uint32_t lds_u32;
   auto read = [&](int ks, Frag& f) {
     const uint32_t st = lbase + (ks % Gm::kStages) * Gm::kStageB;
     // Tile row / column t = 1 is 32 rows further: 4096 B of codes, 256 B of scales.
-    if constexpr (TM == 2) {
-      asm volatile(
-          "ds_read_b128 %0, %12\n"
-          "ds_read_b128 %1, %12 offset:4096\n"
-          "ds_read_b128 %2, %13\n"
-          "ds_read_b128 %3, %13 offset:4096\n"
-          "ds_read_b128 %4, %14\n"
-          "ds_read_b128 %5, %14 offset:4096\n"
-          "ds_read_b128 %6, %15\n"
-          "ds_read_b128 %7, %15 offset:4096\n"
-          "ds_read_b32 %8, %16\n"
-          "ds_read_b32 %9, %16 offset:256\n"
-          "ds_read_b32 %10, %17\n"
-          "ds_read_b32 %11, %17 offset:256\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[1][0]), "=&v"(f.a[1][1]), "=&v"(f.b[0][0]),
-            "=&v"(f.b[0][1]), "=&v"(f.b[1][0]), "=&v"(f.b[1][1]), "=&v"(f.sa[0]), "=&v"(f.sa[1]), "=&v"(f.sb[0]),
-            "=&v"(f.sb[1])
-          : "v"(st + fa0), "v"(st + fa1), "v"(st + fb0), "v"(st + fb1), "v"(st + fsa), "v"(st + fsb)
-          : "memory");
-    } else {
-      asm volatile(
-          "ds_read_b128 %0, %6\n"
-          "ds_read_b128 %1, %7\n"
-          "ds_read_b128 %2, %8\n"
-          "ds_read_b128 %3, %9\n"
-          "ds_read_b32 %4, %10\n"
-          "ds_read_b32 %5, %11\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(f.a[0][0]), "=&v"(f.a[1][0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.sa[0]), "=&v"(f.sb[0])
-          : "v"(st + fa0), "v"(st + fa1), "v"(st + fb0), "v"(st + fb1), "v"(st + fsa), "v"(st + fsb)
-          : "memory");
-    }
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
-      f.sa[t] >>= shift;
-      f.sb[t] >>= shift;
+      f.a[0][t] = *(lds_v4*)(uintptr_t)(st + fa0 + 4096 * t);
+      f.a[1][t] = *(lds_v4*)(uintptr_t)(st + fa1 + 4096 * t);
+      f.b[0][t] = *(lds_v4*)(uintptr_t)(st + fb0 + 4096 * t);
+      f.b[1][t] = *(lds_v4*)(uintptr_t)(st + fb1 + 4096 * t);
+      f.sa[t] = *(lds_u32*)(uintptr_t)(st + fsa + 256 * t);
+      f.sb[t] = *(lds_u32*)(uintptr_t)(st + fsb + 256 * t);
     }
   };
   auto mfma = [&](const Frag& f) {
+    uint32_t sa[TM], sb[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      sa[t] = f.sa[t] >> shift;
+      sb[t] = f.sb[t] >> shift;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TM; ++j) acc[i][j] = mfma_fp4<0>(f.a[0][i], f.b[0][j], acc[i][j], f.sa[i], f.sb[j]);
+      for (int j = 0; j < TM; ++j) acc[i][j] = mfma_fp4<0>(f.a[0][i], f.b[0][j], acc[i][j], sa[i], sb[j]);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TM; ++j) acc[i][j] = mfma_fp4<2>(f.a[1][i], f.b[1][j], acc[i][j], f.sa[i], f.sb[j]);
+      for (int j = 0; j < TM; ++j) acc[i][j] = mfma_fp4<2>(f.a[1][i], f.b[1][j], acc[i][j], sa[i], sb[j]);
+    // The MFMAs are pure operations: without this the compiler sinks them
+    // past the next step's barrier, which serializes the pipeline.
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) asm volatile("" : "+v"(acc[i][j]));
   };
 
-  // Step ks: wait for this wave's loads of step ks (those of the later
+  // sync(ks): wait for this wave's loads of step ks (those of the later
   // steps already issued may stay in flight), barrier (every wave's loads
-  // of step ks have landed, and every wave is done with the stage step
-  // ks - 1 used), refill that stage with step ks + kAhead if there is one.
-  // Group 0 then reads step ks and runs its MFMAs; group 1 first runs the
-  // MFMAs of step ks - 1 from registers and reads step ks last, so that on
-  // each SIMD one wave reads LDS while the other keeps the matrix unit busy.
+  // of step ks have landed), then refill stage (ks + kAhead) % kStages.
+  // That stage last held step ks + kAhead - kStages <= ks - 2, whose
+  // fragments every wave read and consumed (in mfma) before this barrier;
+  // only step ks - 1's reads may still be in flight when the barrier
+  // passes, and its stage is a different one.
   constexpr int LPS = Gm::kLoadsPerStep;
   auto sync = [&](int ks) {
     const int later = min(Gm::kAhead - 1, nk - 1 - ks);  // steps issued after ks
@@ -269,93 +268,48 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   static_assert(Gm::kAhead <= 4, "sync() spells out the wait counts for up to four steps in flight");
   for (int p = 0; p < Gm::kAhead; ++p)
     if (p < nk) issue(p);
-  Frag f;
-  if (grp == 0) {
-    for (int ks = 0; ks < nk; ++ks) {
-      sync(ks);
-      read(ks, f);
-      mfma(f);
-    }
+  // Software pipeline: the fragments of step ks + 1 are read while the
+  // MFMAs of step ks run.  Unrolled by two so that the two fragment sets
+  // keep fixed registers.
+  Frag f0, f1;
+  sync(0);
+  read(0, f0);
+  int ks = 0;
+  for (; ks + 2 < nk; ks += 2) {
+    sync(ks + 1);
+    read(ks + 1, f1);
+    mfma(f0);
+    sync(ks + 2);
+    read(ks + 2, f0);
+    mfma(f1);
+  }
+  if (ks + 1 < nk) {
+    sync(ks + 1);
+    read(ks + 1, f1);
+    mfma(f0);
+    mfma(f1);
   } else {
-    for (int ks = 0; ks < nk; ++ks) {
-      sync(ks);
-      if (ks > 0) mfma(f);
-      read(ks, f);
-    }
-    mfma(f);
+    mfma(f0);
   }
   wait_barrier<0>();
 
-  // Add the two groups' partial tiles through LDS, then write the summed
-  // tile to LDS as fp32 (rows padded): lane (j + 32h) of an MFMA tile holds
-  // rows 8 (r / 4) + 4 h + r % 4 of column j in accumulator register r.
-  f32x4* xch = reinterpret_cast<f32x4*>(L);
-  float* ct = reinterpret_cast<float*>(L);
-  const int partner = wave ^ 4;
-  if constexpr (TM == 2) {
-    // Group g finishes MFMA tile row g and hands tile row 1 - g to its
-    // partner wave.
-    f32x16 give[2], fin[2];
+  // Each K-split group writes its partial tile into its own fp32 region of
+  // LDS (rows padded); the store pass adds the two.  Lane (j + 32h) of an
+  // MFMA tile holds rows 8 (r / 4) + 4 h + r % 4 of column j in accumulator
+  // register r.
+  float* const ct0 = reinterpret_cast<float*>(L);
+  float* const ct1 = ct0 + BT * Gm::kCRow;
+  {
+    float* ct = grp ? ct1 : ct0;
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {  // constant indices keep acc in registers
-      give[jt] = grp ? acc[0][jt] : acc[1][jt];
-      fin[jt] = grp ? acc[1][jt] : acc[0][jt];
-    }
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
+      for (int j = 0; j < TM; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = give[jt][4 * q + e];
-        xch[((wave * 2 + jt) * 4 + q) * 64 + lane] = v;
-      }
-    __syncthreads();
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = xch[((partner * 2 + jt) * 4 + q) * 64 + lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) fin[jt][4 * q + e] += v[e];
-      }
-    __syncthreads();
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 64 * wm + 32 * grp + 8 * (r / 4) + 4 * lh + (r % 4);
-        ct[row * Gm::kCRow + 64 * wn + 32 * jt + li] = fin[jt][r];
-      }
-  } else {
-    // Group g finishes accumulator registers 8 g .. 8 g + 7 and hands the
-    // other eight to its partner.  The halves are picked once, by whole
-    // vectors, so that every register index below is a constant: an index
-    // that depends on the group compiles to a select over all 16 registers
-    // for every element moved (about 1300 instructions, ~4 us per launch).
-    f32x4 keep[2], hand[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = acc[0][0][4 * q + e], hi = acc[0][0][8 + 4 * q + e];
-        keep[q][e] = grp ? hi : lo;
-        hand[q][e] = grp ? lo : hi;
-      }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) xch[(wave * 2 + q) * 64 + lane] = hand[q];
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 2; ++q) keep[q] += xch[(partner * 2 + q) * 64 + lane];
-    __syncthreads();
-    // keep[q][e] is register r = 8 g + 4 q + e: row 16 g + 8 q + 4 h + e.
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 32 * wm + 16 * grp + 8 * q + 4 * lh + e;
-        ct[row * Gm::kCRow + 32 * wn + li] = keep[q][e];
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * TM * wm + 32 * i + 8 * (r / 4) + 4 * lh + (r % 4);
+          ct[row * Gm::kCRow + 32 * TM * wn + 32 * j + li] = acc[i][j][r];
+        }
   }
   __syncthreads();
 
@@ -367,15 +321,27 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   constexpr int kVec = BF16_OUT ? 8 : 4;
   constexpr int kVecPerRow = BT / kVec;
   const bool full = m0 + BT <= M && n0 + BT <= N && (N % kVec) == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15) == 0;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   for (int v = tid; v < BT * kVecPerRow; v += kThreads) {
     const int row = v / kVecPerRow, c0 = (v % kVecPerRow) * kVec;
-    const float* src = ct + row * Gm::kCRow + c0;
+    float src[kVec];
+#pragma unroll
+    for (int q = 0; q < kVec / 4; ++q) {
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(ct0 + row * Gm::kCRow + c0 + 4 * q);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(ct1 + row * Gm::kCRow + c0 + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) src[4 * q + e] = p0[e] + p1[e];
+    }
     const int64_t grow = m0 + row, gcol = n0 + c0;
     if (full) {
       if (BF16_OUT) {
         u32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16_rne(src[2 * e]) | (f32_to_bf16_rne(src[2 * e + 1]) << 16);
+        for (int e = 0; e < 4; ++e) {
+          const f32x2 pr = {src[2 * e], src[2 * e + 1]};
+          o[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+        }
         __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + grow * N + gcol));
       } else {
         const f32x4 o = {src[0], src[1], src[2], src[3]};
