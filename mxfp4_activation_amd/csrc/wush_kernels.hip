@@ -138,6 +138,26 @@ __device__ __forceinline__ float f16_value(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
 
+// fp32(x / 7), the correctly rounded quotient, for finite x >= 0: the
+// product with fp32(1/7) and one FMA correction of its residual.  Equal to
+// the IEEE quotient for every non-negative finite fp32 x, subnormals
+// included (checked exhaustively on the host), at three instructions
+// instead of the ten of a division.
+__device__ __forceinline__ float div7(float x) {
+  constexpr float r = 1.0f / 7.0f;
+  const float q = x * r;
+  return __builtin_fmaf(__builtin_fmaf(-q, 7.0f, x), r, q);
+}
+
+// fp32(1 / s) for s the value of a positive finite fp16 number: the
+// hardware reciprocal with one FMA correction.  Equal to the IEEE quotient
+// for every such s (checked exhaustively on the device against its own
+// division and against the host's).
+__device__ __forceinline__ float recip_f16_value(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  return __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+}
+
 // ---------------------------------------------------------------- scale decisions
 //
 // Each decision is a monotone function of amax.  The checks report whether
@@ -418,7 +438,7 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
     // settled when amax - d and amax + d share sign and exponent field.
     unsure = (__float_as_uint(amax - d) ^ __float_as_uint(amax + d)) > 0x007FFFFFu;
   } else if (FMT == kINT4) {
-    unsure = int4_unsure(amax / 7.0f, d, sdec);
+    unsure = int4_unsure(div7(amax), d, sdec);
   } else {
     unsure = nv_unsure(amax, d, g, sdec);
   }
@@ -455,12 +475,14 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
     // keep the matrix-core values: with the exact scale they can differ
     // from the exactly rounded ones only within the accumulation bound of a
     // rounding midpoint.
+    // Bit r of cand: |y^_r| > lo, the sign of lo - |y^_r| shifted in from
+    // the top (v_alignbit).  The comparison is strict, which still keeps
+    // the output holding the maximum: its |y^| >= amax - 2d > lo since
+    // d > 0.  A settled group's cut is +inf: no candidates.
+    const float lo = unsure ? amax - 2.25f * d : __builtin_inff();
     uint32_t cand = 0u;
-    if (unsure) {
-      const float lo = amax - 2.25f * d;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) cand |= (fabsf(acc[r]) >= lo ? 1u : 0u) << r;
-    }
+    for (int r = 15; r >= 0; --r) cand = __builtin_amdgcn_alignbit(cand, __float_as_uint(lo - fabsf(acc[r])), 31);
     // Both lanes of a token see its 32 candidate bits, output k at bit k:
     // in both halves the swap's first result is the value of lane (n, 0),
     // the second that of lane (n, 1).
@@ -482,7 +504,7 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
       if (unsure) amax = ex;
     }
     // Decide again at the new amax (the same value for the settled groups).
-    if (FMT == kINT4) sdec = f16_bits(amax / 7.0f);
+    if (FMT == kINT4) sdec = f16_bits(div7(amax));
     if (FMT == kNVFP4 && g > 0.0f) sdec = e4m3_code((amax / 6.0f) / g);
   }
   if (FMT == kMXFP4) {
@@ -495,7 +517,8 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
   } else if (FMT == kINT4) {
     const float s = f16_value(sdec);
     scale_bits = sdec;
-    const float r = s > 0.0f ? 1.0f / s : 0.0f;
+    // fp32(1 / s); 0 for a zero or infinite scale
+    const float r = (sdec & 0x7FFFu) != 0u && (sdec & 0x7C00u) != 0x7C00u ? recip_f16_value(s) : 0.0f;
     // With a normal fp16 scale, |y| <= amax and s >= fp32(amax / 7) (1 -
     // 2^-11) give |y r| <= 7.0035 after the roundings of r and of the
     // product: below 7.5, so rounding already lands in [-7, 7].  Zero and
