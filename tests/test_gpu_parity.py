@@ -197,6 +197,42 @@ def test_scale_boundaries_take_exact_path():
     parity.check("int4", xb, tb, c, s)
 
 
+def test_tied_candidates_in_both_lane_halves():
+    """Groups whose maximum is held by several outputs at once, spread over
+    both halves of the 32 outputs (each half lives in a different lane of
+    the pair that owns the token), with near-ties one bf16 step below: every
+    group sits on an E8M0 boundary and has several candidate outputs for
+    the exact step.  Through T = I and through a signed permutation (which
+    moves the tied outputs to other positions and halves), scales must be
+    bit-exact and every group must take the exact step."""
+    G, C, M = 32, 4, 96
+    rng = np.random.default_rng(29)
+    e = rng.integers(-6, 6, (M, C))
+    # every other channel below half the planted maximum 2^e
+    X = rng.uniform(-0.45, 0.45, (M, C * G)) * np.repeat(2.0 ** e, G, axis=1)
+    below = 1.0 - 2.0 ** -8  # one bf16 step below 1
+    for pos, mult in [(2, 1.0), (13, 1.0), (18, 1.0), (29, 1.0), (7, below), (24, below)]:
+        sign = rng.choice([-1.0, 1.0], (M, C))
+        for c in range(C):
+            X[:, c * G + pos] = sign[:, c] * mult * 2.0 ** e[:, c]
+    xb = f64_to_bf16_bits(X)
+    perm = rng.permutation(G)
+    P = np.zeros((G, G))
+    P[np.arange(G), perm] = rng.choice([-1.0, 1.0], G)
+    for T in (np.eye(G), P):
+        tb = f64_to_bf16_bits(np.ascontiguousarray(np.broadcast_to(T, (C, G, G))))
+        c, s, n = _run("mxfp4", xb, tb, n_exact=True)
+        rep = parity.check("mxfp4", xb, tb, c, s)
+        assert n == M * C, (n, M * C)
+        assert rep.n_mismatch == 0
+        for fmt in ("int4", "nvfp4"):
+            Gf = 16 if fmt == "nvfp4" else 32
+            tf = tb if Gf == 32 else f64_to_bf16_bits(np.ascontiguousarray(np.broadcast_to(T[:16, :16], (2 * C, 16, 16))))
+            g = _g_for(xb, tf) if fmt == "nvfp4" else None
+            c, s = _run(fmt, xb, tf, g)
+            parity.check(fmt, xb, tf, c, s, g)
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
 def test_extreme_magnitudes(fmt):
     """Groups of tiny values (bf16 subnormals, E8M0 code 0), huge values (fp16
