@@ -94,13 +94,6 @@ __device__ __forceinline__ float max16(const f32x16& v) {
 
 // ---------------------------------------------------------------- codecs
 
-// E8M0 code of a non-negative finite amax: floor(log2 amax) - 2 + 127,
-// clamped below at 0 (e = -127).  amax < 2^128, so it never exceeds 252.
-__device__ __forceinline__ int e8m0_code(float amax) {
-  int be = (int)(__float_as_uint(amax) >> 23);
-  return be > 2 ? be - 2 : 0;
-}
-
 // E2M1 conversion of a pair: v_cvt_scalef32_pk_fp4_f32 divides both values
 // by 2^(exponent field of `scale`), rounds to nearest even, saturates at +-6,
 // keeps the sign of zero and writes a byte (first value in the low nibble)
@@ -164,10 +157,6 @@ __device__ __forceinline__ float recip_f16_value(float s) {
 // it could change anywhere in [amax - d, amax + d].  When it cannot, the
 // decision at the top of the interval (returned through the reference) is
 // the decision at amax itself, so the caller reuses it.
-
-__device__ __forceinline__ bool mx_unsure(float amax, float d) {
-  return e8m0_code(fmaxf(amax - d, 0.0f)) != e8m0_code(amax + d);
-}
 
 // INT4: q = fp32(amax / 7), the value the fp16 scale rounds; `bits` gets
 // the fp16 scale.
