@@ -167,13 +167,20 @@ __device__ __forceinline__ bool int4_unsure(float q, float d, uint32_t& bits) {
 }
 
 // NVFP4: the E4M3 code of fp32(fp32(amax / 6) / g) goes to `code`.
-__device__ __forceinline__ bool nv_unsure(float amax, float d, float g, uint32_t& code) {
+// The ratio is formed as amax * k6g with k6g = fp32(1 / fp32(6 g)): three
+// roundings, against two in fp32(fp32(amax / 6) / g), so the two differ by
+// at most about 5 * 2^-24 of the ratio.  The interval [ratio - dr,
+// ratio + dr] covers that as well as d; when its two ends share an E4M3
+// code, that code is the one of the exact chain for every amax in
+// [amax - d, amax + d].  No division on this path.
+__device__ __forceinline__ bool nv_unsure(float amax, float d, float g, float k6g, uint32_t& code) {
   code = 0u;
   if (!(g > 0.0f)) return false;  // every code is zero whatever amax is
-  if (amax == 0.0f) return d > 0.0f && e4m3_code((d / 6.0f) / g) != 0u;
-  const float ratio = (amax / 6.0f) / g;
+  if (amax == 0.0f) return d > 0.0f && e4m3_code(d * k6g * (1.0f + 0x1p-20f)) != 0u;
+  const float ratio = amax * k6g;
   // ratio scales linearly with amax; the relative slack covers roundings
-  const float dr = ratio * (d * __builtin_amdgcn_rcpf(amax)) * 1.01f + ratio * 0x1p-20f;
+  // (2^-20) and the ratio's own approximation (2^-21)
+  const float dr = ratio * (d * __builtin_amdgcn_rcpf(amax)) * 1.01f + ratio * (0x1p-20f + 0x1p-21f);
   code = e4m3_code(ratio + dr);
   return e4m3_code(fmaxf(ratio - dr, 0.0f)) != code;
 }
@@ -414,8 +421,9 @@ __device__ __forceinline__ void wg_coords(int n_pg, int n_tg, int token_major, i
 // hold it.
 template <int FMT>
 __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float bound_scale, const Frag& f,
-                                                uint32_t tile, int tile_stride, float g, int lane,
-                                                uint32_t& scale_bits, uint32_t& n_exact) {
+                                                uint32_t tile, int tile_stride, float g, float k6g,
+                                                const float* rtab, int lane, uint32_t& scale_bits,
+                                                uint32_t& n_exact) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   float amax = max_abs16(acc);
   if (G == 32) amax = max_halves(amax);
@@ -429,7 +437,7 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
   } else if (FMT == kINT4) {
     unsure = int4_unsure(div7(amax), d, sdec);
   } else {
-    unsure = nv_unsure(amax, d, g, sdec);
+    unsure = nv_unsure(amax, d, g, k6g, sdec);
   }
   uint64_t pending = __ballot(unsure);
   if (pending) {
@@ -517,11 +525,8 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
     return pack_int4<false>(acc, r);
   } else {
     const uint32_t code = sdec;  // 0 when g <= 0
-    float r = 0.0f;
-    if (g > 0.0f) {
-      float eff = e4m3_value(code) * g;
-      r = eff > 0.0f ? 1.0f / eff : 0.0f;
-    }
+    // fp32(1 / fp32(E4M3(code) g)), or 0: from the workgroup's table
+    const float r = rtab[code];
     scale_bits = code;
     f32x16 v;
 #pragma unroll
@@ -600,6 +605,7 @@ struct QuantLds {
   uint8_t xs[TPW][32 * kXRow];  // activation tiles; codes and scales in place
   float y[kQWaves][32];         // exact-recompute exchange, per wave
   uint32_t red[2][kQWaves];     // AbsMax pass: per-wave maxima of its two reductions
+  float rtab[256];              // NVFP4: fp32(1 / fp32(E4M3(c) g)) for every code c, or 0
 };
 
 // Contract and quantize panel `wave` of one staged tile; write its codes and
@@ -612,7 +618,7 @@ struct QuantLds {
 // an |T| x |x| MFMA, with bscale = 2^-17.
 template <int FMT>
 __device__ __forceinline__ void panel_step(uint8_t* row, const Frag& f, const u32x4& ones, float bscale, float g,
-                                           int wave, int lane, uint32_t& n_exact) {
+                                           float k6g, const float* rtab, int wave, int lane, uint32_t& n_exact) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   const int h = lane >> 5;
   const u32x4 mask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
@@ -647,7 +653,7 @@ __device__ __forceinline__ void panel_step(uint8_t* row, const Frag& f, const u3
   // LDS address of row 0 of the staged tile at this wave's panel: the exact
   // recompute reads a token's channels there.
   const uint32_t tile = (uint32_t)(uintptr_t)(lds_cu8*)(row - (lane & 31) * kXRow + wave * 64);
-  const u32x2 w = quantize_panel<FMT>(acc, bound, bscale, f, tile, kXRow, g, lane, sbits, n_exact);
+  const u32x2 w = quantize_panel<FMT>(acc, bound, bscale, f, tile, kXRow, g, k6g, rtab, lane, sbits, n_exact);
   // Every lane of the wave has read its operands before any lane writes:
   // the reads above feed the MFMAs whose results the writes depend on.
   *reinterpret_cast<u32x2*>(row + wave * 64 + 8 * h) = w;
@@ -821,7 +827,17 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
   u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
   asm volatile("" : "+v"(ones));  // materialized once, kept in VGPRs
   float g = 0.0f;
-  if (FMT == kNVFP4 && !AMAX) g = *a.global_scale;
+  float k6g = 0.0f;
+  if (FMT == kNVFP4 && !AMAX) {
+    g = *a.global_scale;
+    // The decision's ratio factor, and the reciprocals the codes are scaled
+    // by: one IEEE division per thread here instead of one per lane and panel.
+    k6g = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(g > 0.0f ? 1.0f / (6.0f * g) : 0.0f)));
+    if (tid < 256) {
+      const float eff = e4m3_value((uint32_t)tid) * g;
+      L.rtab[tid] = (g > 0.0f && eff > 0.0f) ? 1.0f / eff : 0.0f;
+    }
+  }
 
   // 2. stage, in arrival order
 #pragma unroll
@@ -843,7 +859,7 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       if (!FULL && u >= n_tiles) break;
-      panel_step<FMT>(row + u * (32 * kXRow), f, ones, bscale, g, wave, lane, n_exact);
+      panel_step<FMT>(row + u * (32 * kXRow), f, ones, bscale, g, k6g, L.rtab, wave, lane, n_exact);
     }
   }
   __syncthreads();
