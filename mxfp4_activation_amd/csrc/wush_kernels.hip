@@ -604,7 +604,7 @@ template <int TPW>
 struct QuantLds {
   uint8_t xs[TPW][32 * kXRow];  // activation tiles; codes and scales in place
   float y[kQWaves][32];         // exact-recompute exchange, per wave
-  uint32_t red[2][kQWaves];     // AbsMax pass: per-wave maxima of its two reductions
+  uint32_t red[4][kQWaves];     // AbsMax pass: per-wave maxima of its reductions
   float rtab[256];              // NVFP4: fp32(1 / fp32(E4M3(c) g)) for every code c, or 0
 };
 
@@ -668,7 +668,8 @@ __device__ __forceinline__ void panel_step(uint8_t* row, const Frag& f, const u3
 
 // Largest value of a non-negative float over the workgroup: wave maximum,
 // then one LDS slot per wave.  Every thread gets the result.  Non-negative
-// floats order like their bit patterns.
+// floats order like their bit patterns.  block_max3_nonneg does three at
+// once, behind one barrier.
 __device__ __forceinline__ float block_max_nonneg(float v, uint32_t* slots, int wave, int lane) {
   uint32_t b = __float_as_uint(v);
 #pragma unroll
@@ -682,6 +683,38 @@ __device__ __forceinline__ float block_max_nonneg(float v, uint32_t* slots, int 
 #pragma unroll
   for (int i = 1; i < kQWaves; ++i) r = r > slots[i] ? r : slots[i];
   return __uint_as_float(r);
+}
+
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t b) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t w = (uint32_t)__shfl_xor((int)b, o, 64);
+    b = b > w ? b : w;
+  }
+  return b;
+}
+
+__device__ __forceinline__ void block_max3_nonneg(float& v0, float& v1, float& v2, uint32_t (*slots)[kQWaves], int wave,
+                                                  int lane) {
+  const uint32_t b0 = wave_max_bits(__float_as_uint(v0));
+  const uint32_t b1 = wave_max_bits(__float_as_uint(v1));
+  const uint32_t b2 = wave_max_bits(__float_as_uint(v2));
+  if (lane == 0) {
+    slots[0][wave] = b0;
+    slots[1][wave] = b1;
+    slots[2][wave] = b2;
+  }
+  __syncthreads();
+  uint32_t r0 = slots[0][0], r1 = slots[1][0], r2 = slots[2][0];
+#pragma unroll
+  for (int i = 1; i < kQWaves; ++i) {
+    r0 = r0 > slots[0][i] ? r0 : slots[0][i];
+    r1 = r1 > slots[1][i] ? r1 : slots[1][i];
+    r2 = r2 > slots[2][i] ? r2 : slots[2][i];
+  }
+  v0 = __uint_as_float(r0);
+  v1 = __uint_as_float(r1);
+  v2 = __uint_as_float(r2);
 }
 
 // The exact max |y| over one run of staged tiles (the per-tensor AbsMax
@@ -728,7 +761,18 @@ __device__ __forceinline__ void amax_run(const QuantArgs& a, QuantLds<TPW>& L, F
       hi_t[u] = am + d;
     }
   }
-  const float lo_wg = block_max_nonneg(lo, L.red[0], wave, lane);
+  // The workgroup's largest lower bound, its largest upper bound, and the
+  // largest exact maximum any workgroup has published so far (a relaxed
+  // read; the stored value only grows).  If even the upper bound is below
+  // a published maximum, nothing here can be the tensor's: stop.  The three
+  // are reduced together, so every thread takes the same decision.
+  float hi = 0.0f;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) hi = fmaxf(hi, hi_t[u]);
+  float lo_wg = lo, hi_wg = hi;
+  float cur = __uint_as_float(__hip_atomic_load(a.amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  block_max3_nonneg(lo_wg, hi_wg, cur, L.red, wave, lane);
+  if (hi_wg < cur) return;
 
   float m = 0.0f;
   if (panel_ok) {
@@ -762,7 +806,7 @@ __device__ __forceinline__ void amax_run(const QuantArgs& a, QuantLds<TPW>& L, F
       if ((tokens >> (lane & 31)) & 1u) m = fmaxf(m, max_abs16(acc));
     }
   }
-  const float m_wg = block_max_nonneg(m, L.red[1], wave, lane);
+  const float m_wg = block_max_nonneg(m, L.red[3], wave, lane);
   if (threadIdx.x == 0 && m_wg > 0.0f) {
     const uint32_t w = __float_as_uint(m_wg);
     // The stored value only grows, so a stale read just costs an atomic.
