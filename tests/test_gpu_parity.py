@@ -233,6 +233,27 @@ def test_tied_candidates_in_both_lane_halves():
             parity.check(fmt, xb, tf, c, s, g)
 
 
+@pytest.mark.parametrize("g_mult", [1.0 / 16, 64.0, 0.0])
+def test_nvfp4_static_tensor_scales(g_mult):
+    """NVFP4 with a calibrated (static) tensor scale instead of the data's
+    own: 16x smaller drives block scales into E4M3 saturation, 64x larger
+    into its subnormal codes, and the smallest allowed g (2^-100) saturates
+    every block.  This walks the reciprocal table and the scale decision's
+    approximate ratio across the E4M3 range."""
+    G, C, M = 16, 16, 200
+    rng = np.random.default_rng(37)
+    X = rng.standard_normal((M, C * G)) * (2.0 ** rng.integers(-12, 12, (M, 1)))
+    xb = f64_to_bf16_bits(X)
+    tb = f64_to_bf16_bits(rng.standard_normal((C, G, G)) * 0.25)
+    g = np.float32(_g_for(xb, tb) * g_mult) if g_mult > 0 else np.float32(2.0 ** -100)
+    c, s = _run("nvfp4", xb, tb, g)
+    parity.check("nvfp4", xb, tb, c, s, g)
+    if g_mult > 0:
+        assert np.unique(s).size > 50  # the scales span much of the E4M3 range
+    else:
+        assert (s == 0x7E).all()  # every block at the largest finite E4M3 code
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
 def test_extreme_magnitudes(fmt):
     """Groups of tiny values (bf16 subnormals, E8M0 code 0), huge values (fp16
