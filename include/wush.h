@@ -198,6 +198,43 @@ wush_status wush_gptq_block(int fmt, const double* Wbar, const double* R, int G,
                             void* codes, int64_t codes_stride, void* scales, int64_t scales_stride,
                             hipStream_t stream);
 
+/* GPTQ-WUSH, the whole of Algorithm 1 for one layer ("WUSH", deep dive,
+ * section 3.4.6, "GPTQ Integration (Algorithm 1)"), in float64 on the device:
+ *   1. Hx = Xcal^T Xcal / n_cal + damp * mean(diag) * I;  X' = its lower
+ *      Cholesky factor.
+ *   2. Y = W X'.
+ *   3. For blocks b = d_in/G - 1 down to 0 (columns [bG, bG + G)):
+ *        Y_b = U S V^T (thin SVD; singular values descending; each (u_k, v_k)
+ *        signed so that v_k's largest-magnitude entry is positive, ties to
+ *        the lowest index);  S <- S / sqrt(d_out);
+ *        T_x[b] = H S^1/2 V^T X'[b,b]^-1           (activation transform);
+ *        Wbar   = sqrt(d_out) H S^1/2 U^T            ([G][d_out]);
+ *        each output channel's G values of Wbar are one group, quantized
+ *        as in wush_gptq_block with R the upper Cholesky factor of
+ *        (H S H^T)^-1 (use_gptq != 0) or R = I (round-to-nearest);
+ *        Y[:, < bG] -= Wsub^T T_x[b] X'[b, < bG], Wsub = the quantized
+ *        block (GPTQ) or Wbar (round-to-nearest).
+ *      H is the Sylvester Hadamard matrix / sqrt(G).
+ *   fmt: 0 = MXFP4, 2 = INT4.  G: 16 or 32, dividing d_in.  damp >= 0 (the
+ *   relative damping; 0.01 is GPTQ's customary value).
+ *   Inputs:  W float64 [d_out][d_in] (nn.Linear order); Xcal float64
+ *            [n_cal][d_in].
+ *   Outputs: Xp  float64 [d_in][d_in], the lower factor X' (zero above the
+ *                diagonal);
+ *            Y   float64 [d_out][d_in], column block b = the target block b
+ *                was fitted to (W X' less the updates of blocks above b);
+ *            T_x float64 [d_in/G][G][G]; Wq float64 [d_out][d_in], the
+ *                dequantized weights (block b in columns b);
+ *            codes u8 [d_out][d_in/2] (4-byte aligned), scales [d_out][d_in/G]
+ *                (E8M0 bytes, or fp16 bits 2-byte aligned): the layout
+ *                wush_gemm_mxfp4 and wush_dequant read.
+ *   Float64 arrays 8-byte aligned; outputs must not overlap inputs or each
+ *   other.  A Hessian that is not positive definite after damping yields
+ *   NaN.  Errors as for wush_quant. */
+wush_status wush_gptq_wush(int fmt, const double* W, const double* Xcal, int64_t d_out, int64_t n_cal, int64_t d_in,
+                           int G, double damp, int use_gptq, double* Xp, double* Y, double* T_x, double* Wq,
+                           void* codes, void* scales, hipStream_t stream);
+
 /* Transform only: Y[m][cG+i] = sum_j T[c][i][j] x_(cG+j), in fp32 from the
  * matrix cores, without rounding fix-up.  G is 16 or 32.  Use it to check
  * values before quantization, or when the transformed activations are wanted

@@ -442,6 +442,56 @@ wush_status wush_gptq_block(int fmt, const double* Wbar, const double* R, int G,
   return WUSH_OK;
 }
 
+wush_status wush_gptq_wush(int fmt, const double* W, const double* Xcal, int64_t d_out, int64_t n_cal, int64_t d_in,
+                           int G, double damp, int use_gptq, double* Xp, double* Y, double* T_x, double* Wq,
+                           void* codes, void* scales, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (fmt != 0 && fmt != 2) return fail(WUSH_EUNSUPPORTED, "GPTQ-WUSH supports MXFP4 (0) and INT4 (2), got %d", fmt);
+  if (G != 16 && G != 32) return fail(WUSH_EUNSUPPORTED, "G must be 16 or 32 (got %d)", G);
+  if (d_in <= 0 || d_in % G != 0) return fail(WUSH_EINVAL, "d_in must be a positive multiple of %d (got %lld)", G,
+                                              (long long)d_in);
+  if (d_out <= 0 || n_cal <= 0) return fail(WUSH_EINVAL, "d_out and n_cal must be >= 1");
+  if (d_in > ((int64_t)1 << 16) || d_out > ((int64_t)1 << 24) || n_cal > ((int64_t)1 << 30) ||
+      d_out * d_in > ((int64_t)1 << 31) || n_cal * d_in > ((int64_t)1 << 36))
+    return fail(WUSH_EINVAL, "sizes too large");
+  if (!(damp >= 0.0) || damp > 1e30) return fail(WUSH_EINVAL, "damp must be finite and >= 0");
+  if (!W || !Xcal || !Xp || !Y || !T_x || !Wq || !codes || !scales) return fail(WUSH_EINVAL, "null pointer");
+  if (!aligned(W, 8) || !aligned(Xcal, 8) || !aligned(Xp, 8) || !aligned(Y, 8) || !aligned(T_x, 8) || !aligned(Wq, 8))
+    return fail(WUSH_EALIGN, "float64 arrays must be 8-byte aligned");
+  if (!aligned(codes, 4)) return fail(WUSH_EALIGN, "codes must be 4-byte aligned");
+  if (fmt == 2 && !aligned(scales, 2)) return fail(WUSH_EALIGN, "INT4 scales must be 2-byte aligned");
+  const uint64_t nw = (uint64_t)d_out * d_in * 8, nx = (uint64_t)n_cal * d_in * 8, nh = (uint64_t)d_in * d_in * 8;
+  const uint64_t nt = (uint64_t)d_in * G * 8, nc = (uint64_t)d_out * d_in / 2;
+  const uint64_t ns = (uint64_t)d_out * (d_in / G) * (fmt == 2 ? 2 : 1);
+  const void* outs[6] = {Xp, Y, T_x, Wq, codes, scales};
+  const uint64_t nout[6] = {nh, nw, nt, nw, nc, ns};
+  for (int i = 0; i < 6; ++i) {
+    if (overlap(outs[i], nout[i], W, nw) || overlap(outs[i], nout[i], Xcal, nx))
+      return fail(WUSH_EINVAL, "an output overlaps an input");
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(outs[i], nout[i], outs[j], nout[j])) return fail(WUSH_EINVAL, "two outputs overlap");
+  }
+  wush_status st = check_device();
+  if (st != WUSH_OK) return st;
+  wush::GptqWushArgs a{};
+  a.W = W;
+  a.Xcal = Xcal;
+  a.d_out = d_out;
+  a.n_cal = n_cal;
+  a.d_in = d_in;
+  a.damp = damp;
+  a.use_gptq = use_gptq ? 1 : 0;
+  a.Xp = Xp;
+  a.Y = Y;
+  a.T_x = T_x;
+  a.Wq = Wq;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.scales = scales;
+  hipError_t e = wush::launch_gptq_wush(fmt, G, a, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
 wush_status wush_fixed_transforms(int kind, int64_t C, int G, double* T, void* T_bf16, hipStream_t stream) {
   g_last_error[0] = 0;
   if (kind != 0 && kind != 1) return fail(WUSH_EINVAL, "kind must be 0 (identity) or 1 (Hadamard), got %d", kind);

@@ -210,6 +210,28 @@ static void other_entries() {
   REJECT(q(0, 32, 8, 18, 3 * B), WUSH_EALIGN);
   REJECT(q(0, 32, 8, 16, B), WUSH_EINVAL);
   ACCEPT(q(2, 32, 8, 16, 3 * B), 1);
+
+  // GPTQ-WUSH: W, Xcal inputs; Xp, Y, T_x, Wq, codes, scales outputs, each
+  // far from the others.
+  auto gw = [](int fmt, int G, int64_t dout, int64_t n, int64_t din, double damp, uintptr_t xp, uintptr_t cd,
+               uintptr_t sc) {
+    return wush_gptq_wush(fmt, static_cast<const double*>(P(A)), static_cast<const double*>(P(2 * A)), dout, n, din,
+                          G, damp, 1, static_cast<double*>(P(xp)), static_cast<double*>(P(2 * B)),
+                          static_cast<double*>(P(3 * B)), static_cast<double*>(P(4 * B)), P(cd), P(sc), nullptr);
+  };
+  REJECT(gw(1, 32, 8, 16, 64, 0.01, B, 5 * B, 6 * B), WUSH_EUNSUPPORTED);
+  REJECT(gw(0, 24, 8, 16, 48, 0.01, B, 5 * B, 6 * B), WUSH_EUNSUPPORTED);
+  REJECT(gw(0, 32, 8, 16, 48, 0.01, B, 5 * B, 6 * B), WUSH_EINVAL);
+  REJECT(gw(0, 32, 0, 16, 64, 0.01, B, 5 * B, 6 * B), WUSH_EINVAL);
+  REJECT(gw(0, 32, 8, 0, 64, 0.01, B, 5 * B, 6 * B), WUSH_EINVAL);
+  REJECT(gw(0, 32, 8, 16, 64, -1.0, B, 5 * B, 6 * B), WUSH_EINVAL);
+  REJECT(gw(0, 32, 8, 16, 64, 0.01, B + 4, 5 * B, 6 * B), WUSH_EALIGN);
+  REJECT(gw(0, 32, 8, 16, 64, 0.01, B, 5 * B + 2, 6 * B), WUSH_EALIGN);
+  REJECT(gw(2, 32, 8, 16, 64, 0.01, B, 5 * B, 6 * B + 1), WUSH_EALIGN);
+  REJECT(gw(0, 32, 8, 16, 64, 0.01, B, 2 * B, 6 * B), WUSH_EINVAL);  // codes over Y
+  REJECT(gw(0, 32, 8, 16, 64, 0.01, A, 5 * B, 6 * B), WUSH_EINVAL);  // Xp over W
+  ACCEPT(gw(0, 32, 8, 16, 64, 0.01, B, 5 * B, 6 * B), 1);
+  ACCEPT(gw(2, 16, 8, 16, 64, 0.0, B, 5 * B, 6 * B), 1);
 }
 
 int main() {

@@ -70,5 +70,6 @@ hipError_t launch_build(int, const BuildArgs&, hipStream_t) { ++g_launches; retu
 hipError_t launch_fixed(int, int64_t, int, double*, uint16_t*, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_f64_to_bf16(const double*, int64_t, uint16_t*, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_gptq_block(int, int, const GptqArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_gptq_wush(int, int, const GptqWushArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 
 }  // namespace wush

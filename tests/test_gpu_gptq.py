@@ -4,11 +4,14 @@
   on the same float64 inputs: both run the same float64 operations in the
   same order (no contraction), so codes, scales and dequantized values must
   match bit for bit.  R = I must give round-to-nearest.
-* The whole algorithm (torch float64 on the device + the kernel) against
-  the oracle (LAPACK): the activation transforms within 1e-8 of the block's
-  largest entry, at most 1e-3 of the weight codes one level apart (a code
-  can flip where the two SVD routes put a value within rounding of a
-  midpoint), and the calibration error of the quantized layer within 1%.
+* The whole algorithm in the library (wush_gptq_wush: blocked Cholesky,
+  float64 GEMMs, the block's SVD through its Gram matrix, the intra-block
+  step) against the oracle (LAPACK): the activation transforms within 1e-8
+  of the block's largest entry, at most 1e-3 of the weight codes one level
+  apart (a code can flip where the two SVD routes put a value within
+  rounding of a midpoint), and the calibration error of the quantized layer
+  within 1%.  Its Cholesky factor against LAPACK's on the same damped
+  Hessian, and the upper triangle exactly zero.
 * Eq. 10 end to end on the device: activations through the fused kernel
   with the GPTQ-WUSH transforms, weights from GPTQ-WUSH, the MXFP4 GEMM;
   GPTQ gives a lower output error than round-to-nearest in the same
@@ -75,13 +78,15 @@ def test_gptq_block_kernel_bit_exact(fmt, G, d_out):
     np.testing.assert_array_equal(c2, codecs.pack_nibbles(rc2.T))
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "int4"])
-def test_gptq_wush_matches_oracle(fmt):
+@pytest.mark.parametrize("fmt,G,mode", [("mxfp4", 32, True), ("int4", 32, True), ("mxfp4", 16, False),
+                                        ("int4", 16, True), ("mxfp4", 32, False)])
+def test_gptq_wush_matches_oracle(fmt, G, mode):
     from mxfp4_activation_amd import gptq as pg
 
+    print("case", fmt, G, mode, flush=True)
     W, Xc, _ = gen_linear_layer(256, 96, 1024, 1, seed=12, n_outlier=3)
-    ref = gptq.gptq_wush_ref(W, Xc, 32, fmt, gptq=True)
-    got = pg.gptq_wush(torch.from_numpy(W).cuda(), torch.from_numpy(Xc).cuda(), 32, fmt, gptq=True)
+    ref = gptq.gptq_wush_ref(W, Xc, G, fmt, gptq=mode)
+    got = pg.gptq_wush(torch.from_numpy(W).cuda(), torch.from_numpy(Xc).cuda(), G, fmt, gptq=mode)
     torch.cuda.synchronize()
     tx = got.T_x.cpu().numpy()
     scale = np.abs(ref.T_x).max(axis=(1, 2), keepdims=True)
@@ -93,6 +98,27 @@ def test_gptq_wush_matches_oracle(fmt):
     res = gptq.GptqWush(tx, got.Wq.cpu().numpy(), None, None)
     e_got = np.mean((gptq.layer_output(res, Xc, lambda v: v) - Xc @ W.T) ** 2)
     assert e_got == pytest.approx(e_ref, rel=1e-2)
+
+
+def test_gptq_wush_cholesky_factor():
+    """The library's blocked Cholesky of the damped Hessian against LAPACK's
+    on the same float64 Hessian (a library routine on the definition, not
+    the oracle): lower factors within 1e-10 of the largest entry, zero above
+    the diagonal, over 13 panels and GEMM tiles cut by the matrix edge."""
+    from mxfp4_activation_amd import gptq as pg
+
+    W, Xc, _ = gen_linear_layer(208, 40, 700, 1, seed=21, n_outlier=2)
+    got = pg.gptq_wush(torch.from_numpy(W).cuda(), torch.from_numpy(Xc).cuda(), 16, "mxfp4", gptq=True)
+    torch.cuda.synchronize()
+    Hx = Xc.T @ Xc / Xc.shape[0]
+    Hx = Hx + gptq.DEFAULT_GPTQ_DAMP * np.mean(np.diag(Hx)) * np.eye(Hx.shape[0])
+    Lref = np.linalg.cholesky(Hx)
+    Xp = got.Xp.cpu().numpy()
+    assert np.all(np.triu(Xp, 1) == 0.0)
+    assert np.abs(Xp - Lref).max() <= 1e-10 * np.abs(Lref).max()
+    # The last block's target is W X' itself (no block above it).
+    Y = got.Y.cpu().numpy()
+    np.testing.assert_allclose(Y[:, -16:], (W @ Lref)[:, -16:], rtol=0, atol=1e-10 * np.abs(W @ Lref).max())
 
 
 def test_eq10_forward_with_gptq_weights():
