@@ -215,8 +215,9 @@ wush_status wush_gptq_block(int fmt, const double* Wbar, const double* R, int G,
  *        Y[:, < bG] -= Wsub^T T_x[b] X'[b, < bG], Wsub = the quantized
  *        block (GPTQ) or Wbar (round-to-nearest).
  *      H is the Sylvester Hadamard matrix / sqrt(G).
- *   fmt: 0 = MXFP4, 2 = INT4.  G: 16 or 32, dividing d_in.  damp >= 0 (the
- *   relative damping; 0.01 is GPTQ's customary value).
+ *   fmt: 0 = MXFP4, 2 = INT4.  G: 16 or 32, dividing d_in.  d_out >= G,
+ *   n_cal >= 1.  damp >= 0 (the relative damping; 0.01 is GPTQ's customary
+ *   value).
  *   Inputs:  W float64 [d_out][d_in] (nn.Linear order); Xcal float64
  *            [n_cal][d_in].
  *   Outputs: Xp  float64 [d_in][d_in], the lower factor X' (zero above the
@@ -229,7 +230,8 @@ wush_status wush_gptq_block(int fmt, const double* Wbar, const double* R, int G,
  *                (E8M0 bytes, or fp16 bits 2-byte aligned): the layout
  *                wush_gemm_mxfp4 and wush_dequant read.
  *   Float64 arrays 8-byte aligned; outputs must not overlap inputs or each
- *   other.  A Hessian that is not positive definite after damping yields
+ *   other.  A Hessian that is not positive definite after damping, or (with
+ *   use_gptq) a block whose target Y_b has a zero singular value, yields
  *   NaN.  Errors as for wush_quant. */
 wush_status wush_gptq_wush(int fmt, const double* W, const double* Xcal, int64_t d_out, int64_t n_cal, int64_t d_in,
                            int G, double damp, int use_gptq, double* Xp, double* Y, double* T_x, double* Wq,

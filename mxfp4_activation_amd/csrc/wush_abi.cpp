@@ -450,7 +450,7 @@ wush_status wush_gptq_wush(int fmt, const double* W, const double* Xcal, int64_t
   if (G != 16 && G != 32) return fail(WUSH_EUNSUPPORTED, "G must be 16 or 32 (got %d)", G);
   if (d_in <= 0 || d_in % G != 0) return fail(WUSH_EINVAL, "d_in must be a positive multiple of %d (got %lld)", G,
                                               (long long)d_in);
-  if (d_out <= 0 || n_cal <= 0) return fail(WUSH_EINVAL, "d_out and n_cal must be >= 1");
+  if (d_out < G || n_cal <= 0) return fail(WUSH_EINVAL, "d_out must be >= G and n_cal >= 1");
   if (d_in > ((int64_t)1 << 16) || d_out > ((int64_t)1 << 24) || n_cal > ((int64_t)1 << 30) ||
       d_out * d_in > ((int64_t)1 << 31) || n_cal * d_in > ((int64_t)1 << 36))
     return fail(WUSH_EINVAL, "sizes too large");

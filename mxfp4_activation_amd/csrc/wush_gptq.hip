@@ -441,7 +441,8 @@ __global__ __launch_bounds__(256) void gptq_wush_block_kernel(GptqWushArgs a, in
       double pl = 0.0;
       for (int j = 0; j < G; ++j) pl = fma(P[k][j], L.Li[j][l], pl);
       tv = fma(h * rs, pl, tv);
-      mv = fma(h * (rs / L.sk[k]), P[k][l], mv);
+      // A zero singular value contributes nothing to Wbar (S^1/2 U^T).
+      mv = fma(h * (L.sk[k] > 0.0 ? rs / L.sk[k] : 0.0), P[k][l], mv);
       hv = fma(h / sn, hadamard_entry<G>(l, k), hv);
     }
     L.T[r][l] = tv;

@@ -219,19 +219,20 @@ static void other_entries() {
                           G, damp, 1, static_cast<double*>(P(xp)), static_cast<double*>(P(2 * B)),
                           static_cast<double*>(P(3 * B)), static_cast<double*>(P(4 * B)), P(cd), P(sc), nullptr);
   };
-  REJECT(gw(1, 32, 8, 16, 64, 0.01, B, 5 * B, 6 * B), WUSH_EUNSUPPORTED);
-  REJECT(gw(0, 24, 8, 16, 48, 0.01, B, 5 * B, 6 * B), WUSH_EUNSUPPORTED);
-  REJECT(gw(0, 32, 8, 16, 48, 0.01, B, 5 * B, 6 * B), WUSH_EINVAL);
+  REJECT(gw(1, 32, 40, 16, 64, 0.01, B, 5 * B, 6 * B), WUSH_EUNSUPPORTED);
+  REJECT(gw(0, 24, 40, 16, 48, 0.01, B, 5 * B, 6 * B), WUSH_EUNSUPPORTED);
+  REJECT(gw(0, 32, 40, 16, 48, 0.01, B, 5 * B, 6 * B), WUSH_EINVAL);
   REJECT(gw(0, 32, 0, 16, 64, 0.01, B, 5 * B, 6 * B), WUSH_EINVAL);
-  REJECT(gw(0, 32, 8, 0, 64, 0.01, B, 5 * B, 6 * B), WUSH_EINVAL);
-  REJECT(gw(0, 32, 8, 16, 64, -1.0, B, 5 * B, 6 * B), WUSH_EINVAL);
-  REJECT(gw(0, 32, 8, 16, 64, 0.01, B + 4, 5 * B, 6 * B), WUSH_EALIGN);
-  REJECT(gw(0, 32, 8, 16, 64, 0.01, B, 5 * B + 2, 6 * B), WUSH_EALIGN);
-  REJECT(gw(2, 32, 8, 16, 64, 0.01, B, 5 * B, 6 * B + 1), WUSH_EALIGN);
-  REJECT(gw(0, 32, 8, 16, 64, 0.01, B, 2 * B, 6 * B), WUSH_EINVAL);  // codes over Y
-  REJECT(gw(0, 32, 8, 16, 64, 0.01, A, 5 * B, 6 * B), WUSH_EINVAL);  // Xp over W
-  ACCEPT(gw(0, 32, 8, 16, 64, 0.01, B, 5 * B, 6 * B), 1);
-  ACCEPT(gw(2, 16, 8, 16, 64, 0.0, B, 5 * B, 6 * B), 1);
+  REJECT(gw(0, 32, 31, 16, 64, 0.01, B, 5 * B, 6 * B), WUSH_EINVAL);  // d_out < G
+  REJECT(gw(0, 32, 40, 0, 64, 0.01, B, 5 * B, 6 * B), WUSH_EINVAL);
+  REJECT(gw(0, 32, 40, 16, 64, -1.0, B, 5 * B, 6 * B), WUSH_EINVAL);
+  REJECT(gw(0, 32, 40, 16, 64, 0.01, B + 4, 5 * B, 6 * B), WUSH_EALIGN);
+  REJECT(gw(0, 32, 40, 16, 64, 0.01, B, 5 * B + 2, 6 * B), WUSH_EALIGN);
+  REJECT(gw(2, 32, 40, 16, 64, 0.01, B, 5 * B, 6 * B + 1), WUSH_EALIGN);
+  REJECT(gw(0, 32, 40, 16, 64, 0.01, B, 2 * B, 6 * B), WUSH_EINVAL);  // codes over Y
+  REJECT(gw(0, 32, 40, 16, 64, 0.01, A, 5 * B, 6 * B), WUSH_EINVAL);  // Xp over W
+  ACCEPT(gw(0, 32, 40, 16, 64, 0.01, B, 5 * B, 6 * B), 1);
+  ACCEPT(gw(2, 16, 16, 16, 64, 0.0, B, 5 * B, 6 * B), 1);
 }
 
 int main() {
