@@ -151,6 +151,30 @@ def test_gptq_block_validation():
     assert g(0, 32, 8, c=B) == _lib.WUSH_EINVAL  # codes overlap Q
 
 
+def test_gptq_wush_validation():
+    """GPTQ-WUSH rejects bad formats, shapes, damping, alignment and
+    overlapping buffers before any HIP call (fake device addresses)."""
+    lib = wush.load()
+    B = A * 64
+
+    def g(fmt=0, G=32, d_out=40, n=16, d_in=64, damp=0.01, xp=B, codes=B * 5, scales=B * 6):
+        return lib.wush_gptq_wush(fmt, A, A * 2, d_out, n, d_in, G, damp, 1, xp, B * 2, B * 3, B * 4, codes,
+                                  scales, None)
+
+    assert g(fmt=1) == _lib.WUSH_EUNSUPPORTED  # NVFP4 not offered
+    assert g(G=24, d_in=48) == _lib.WUSH_EUNSUPPORTED
+    assert g(d_in=48) == _lib.WUSH_EINVAL  # G does not divide d_in
+    assert g(d_out=31) == _lib.WUSH_EINVAL  # a block's thin SVD needs G rows
+    assert g(n=0) == _lib.WUSH_EINVAL
+    assert g(damp=-1.0) == _lib.WUSH_EINVAL
+    assert g(damp=float("nan")) == _lib.WUSH_EINVAL
+    assert g(xp=B + 4) == _lib.WUSH_EALIGN
+    assert g(codes=B * 5 + 2) == _lib.WUSH_EALIGN
+    assert g(fmt=2, scales=B * 6 + 1) == _lib.WUSH_EALIGN
+    assert g(codes=B * 2) == _lib.WUSH_EINVAL  # codes overlap Y
+    assert g(xp=A) == _lib.WUSH_EINVAL  # X' overlaps W
+
+
 def test_support_entry_validation():
     lib = wush.load()
     B = A * 64
