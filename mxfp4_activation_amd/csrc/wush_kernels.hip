@@ -452,7 +452,10 @@ __device__ __forceinline__ u32x2 quantize_panel(f32x16& acc, float bound, float 
     // land here: the bound's 2^-120 term leaves their interval across
     // several E8M0 codes.  (The INT4 and NVFP4 decisions are already
     // settled for them: fp16 and E4M3 both round that interval to 0.)
-    if (FMT == kMXFP4) {
+    // Such a token's group has amax = 0, so the check (an LDS re-read) runs
+    // only when an unsure group has amax = 0; it cost about 0.24 us per
+    // 4096 x 4096 launch when it ran in every recompute.
+    if (FMT == kMXFP4 && __ballot(unsure && amax == 0.0f)) {
       const u32x4 q0 = *reinterpret_cast<lds_u32x4*>((lds_cu8*)(uintptr_t)xo);
       const u32x4 q1 = *reinterpret_cast<lds_u32x4*>((lds_cu8*)(uintptr_t)(xo + 32));
       const uint32_t any = (q0[0] | q0[1] | q0[2] | q0[3] | q1[0] | q1[1] | q1[2] | q1[3]) & 0x7FFF7FFFu;
