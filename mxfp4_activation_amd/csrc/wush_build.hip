@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include "wush_build.h"
+#include "wush_f64_block.h"
 
 namespace wush {
 namespace {
@@ -38,13 +39,6 @@ __device__ __forceinline__ double bf16_to_f64(uint16_t b) { return (double)__uin
 __device__ __forceinline__ uint16_t f64_to_bf16_via_f32(double v) {
   const uint32_t b = __float_as_uint((float)v);  // round to nearest even
   return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-}
-
-// Sylvester Hadamard entry, normalized.
-template <int G>
-__device__ __forceinline__ double hadamard(int a, int k) {
-  const double h = 1.0 / sqrt((double)G);
-  return (__builtin_popcount((unsigned)(a & k)) & 1) ? -h : h;
 }
 
 template <int G>
@@ -153,60 +147,8 @@ __global__ __launch_bounds__(kThreads) void build_kernel(BuildArgs a) {
     L.V[i][j] = i == j ? 1.0 : 0.0;
   }
 
-  // One-sided Jacobi on the columns of A.  Round r pairs column
-  // (r + k) % (G - 1) with (r - k) % (G - 1) for k = 1 .. G/2 - 1 and
-  // r % (G - 1) with G - 1 (k = 0): every pair once per sweep.  Pair k is
-  // handled by threads [k * G/2, (k + 1) * G/2), two rows each.
-  constexpr int kTpp = G / 2;
-  const int pk = t / kTpp, pl = t % kTpp;
-  const bool in_pair = pk < G / 2;
-  for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-    if (t == 0) L.rotated = 0;
-    for (int r = 0; r < G - 1; ++r) {
-      __syncthreads();
-      if (in_pair) {
-        int p, q;
-        if (pk == 0) {
-          p = r % (G - 1);
-          q = G - 1;
-        } else {
-          p = (r + pk) % (G - 1);
-          q = (r - pk + (G - 1)) % (G - 1);
-        }
-        const int r0 = 2 * pl, r1 = 2 * pl + 1;
-        double al = L.A[r0][p] * L.A[r0][p] + L.A[r1][p] * L.A[r1][p];
-        double be = L.A[r0][q] * L.A[r0][q] + L.A[r1][q] * L.A[r1][q];
-        double ga = L.A[r0][p] * L.A[r0][q] + L.A[r1][p] * L.A[r1][q];
-#pragma unroll
-        for (int o = 1; o < kTpp; o <<= 1) {
-          al += __shfl_xor(al, o, kTpp);
-          be += __shfl_xor(be, o, kTpp);
-          ga += __shfl_xor(ga, o, kTpp);
-        }
-        // Rotate when the pair is not orthogonal to rounding level.
-        if (fabs(ga) > 1e-15 * sqrt(al * be) && ga != 0.0) {
-          const double zeta = (be - al) / (2.0 * ga);
-          const double tn = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
-          const double cs = 1.0 / sqrt(1.0 + tn * tn), sn = cs * tn;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int rw = 2 * pl + h;
-            const double xp = L.A[rw][p], xq = L.A[rw][q];
-            L.A[rw][p] = cs * xp - sn * xq;
-            L.A[rw][q] = sn * xp + cs * xq;
-            const double vp = L.V[rw][p], vq = L.V[rw][q];
-            L.V[rw][p] = cs * vp - sn * vq;
-            L.V[rw][q] = sn * vp + cs * vq;
-          }
-          if (pl == 0) L.rotated = 1;
-        }
-      }
-    }
-    __syncthreads();
-    const int any = L.rotated;
-    __syncthreads();
-    if (!any) break;
-  }
+  // SVD of M by one-sided Jacobi on its columns: M V = U S.
+  jacobi_columns<G>(L.A, L.V, &L.rotated, kMaxSweeps);
 
   // Singular values (column norms), descending order, sign rule.
   if (t < G) {
@@ -258,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void build_kernel(BuildArgs a) {
     const int aa = e / G, l = e % G;
     double tw = 0.0, tx = 0.0;
     for (int k = 0; k < G; ++k) {
-      const double h = a.use_hadamard ? hadamard<G>(aa, k) : (aa == k ? 1.0 : 0.0);
+      const double h = a.use_hadamard ? hadamard_entry<G>(aa, k) : (aa == k ? 1.0 : 0.0);
       if (h == 0.0) continue;
       double qw = 0.0, qx = 0.0;
       for (int j = 0; j <= l; ++j) {
@@ -283,7 +225,7 @@ __global__ void fixed_kernel(int kind, int64_t n, double* T, uint16_t* T_bf16) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n) return;
   const int i = (int)((e / G) % G), j = (int)(e % G);
-  const double v = kind ? hadamard<G>(i, j) : (i == j ? 1.0 : 0.0);
+  const double v = kind ? hadamard_entry<G>(i, j) : (i == j ? 1.0 : 0.0);
   if (T) T[e] = v;
   if (T_bf16) T_bf16[e] = f64_to_bf16_via_f32(v);
 }

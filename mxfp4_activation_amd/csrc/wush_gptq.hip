@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "wush_f64_block.h"
 #include "wush_gptq.h"
 
 namespace wush {
@@ -263,12 +264,6 @@ __global__ void zero_upper_kernel(double* H, int64_t n) {
 // ---------------------------------------------------------------- one block of Algorithm 1
 
 template <int G>
-__device__ __forceinline__ double hadamard_entry(int a, int k) {
-  const double h = 1.0 / sqrt((double)G);
-  return (__builtin_popcount((unsigned)(a & k)) & 1) ? -h : h;
-}
-
-template <int G>
 struct BlockLds {
   double rows[64][G + 1];  // Gram staging
   double A[G][G + 1];      // Gram matrix, rotated by one-sided Jacobi
@@ -322,62 +317,9 @@ __global__ __launch_bounds__(256) void gptq_wush_block_kernel(GptqWushArgs a, in
   }
 
   // 2. One-sided Jacobi on the columns of the (symmetric, positive
-  // semi-definite) Gram matrix: on convergence its columns are orthogonal,
-  // V holds the eigenvectors and the column norms are the eigenvalues.
-  // Round r pairs column (r + k) % (G - 1) with (r - k) % (G - 1) for
-  // k = 1 .. G/2 - 1 and r % (G - 1) with G - 1 (k = 0).
-  {
-    constexpr int kTpp = G / 2;
-    const int pk = t / kTpp, pl = t % kTpp;
-    const bool in_pair = pk < G / 2;
-    for (int sweep = 0; sweep < 40; ++sweep) {
-      __syncthreads();
-      if (t == 0) L.rotated = 0;
-      for (int r = 0; r < G - 1; ++r) {
-        __syncthreads();
-        if (in_pair) {
-          int p, q;
-          if (pk == 0) {
-            p = r % (G - 1);
-            q = G - 1;
-          } else {
-            p = (r + pk) % (G - 1);
-            q = (r - pk + (G - 1)) % (G - 1);
-          }
-          const int r0 = 2 * pl, r1 = 2 * pl + 1;
-          double al = L.A[r0][p] * L.A[r0][p] + L.A[r1][p] * L.A[r1][p];
-          double be = L.A[r0][q] * L.A[r0][q] + L.A[r1][q] * L.A[r1][q];
-          double ga = L.A[r0][p] * L.A[r0][q] + L.A[r1][p] * L.A[r1][q];
-#pragma unroll
-          for (int o = 1; o < kTpp; o <<= 1) {
-            al += __shfl_xor(al, o, kTpp);
-            be += __shfl_xor(be, o, kTpp);
-            ga += __shfl_xor(ga, o, kTpp);
-          }
-          if (fabs(ga) > 1e-15 * sqrt(al * be) && ga != 0.0) {
-            const double zeta = (be - al) / (2.0 * ga);
-            const double tn = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
-            const double cs = 1.0 / sqrt(1.0 + tn * tn), sn = cs * tn;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int rw = 2 * pl + h;
-              const double xp = L.A[rw][p], xq = L.A[rw][q];
-              L.A[rw][p] = cs * xp - sn * xq;
-              L.A[rw][q] = sn * xp + cs * xq;
-              const double vp = L.V[rw][p], vq = L.V[rw][q];
-              L.V[rw][p] = cs * vp - sn * vq;
-              L.V[rw][q] = sn * vp + cs * vq;
-            }
-            if (pl == 0) L.rotated = 1;
-          }
-        }
-      }
-      __syncthreads();
-      const int any = L.rotated;
-      if (!any) break;
-    }
-  }
-  __syncthreads();
+  // semi-definite) Gram matrix: its columns end orthogonal, V holds the
+  // eigenvectors and the column norms are the eigenvalues.
+  jacobi_columns<G>(L.A, L.V, &L.rotated, 40);
 
   // 3. Eigenvalues (column norms), descending order; X'[b, b]^-1 by forward
   // substitution, one column per thread.
