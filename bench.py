@@ -876,20 +876,30 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _code_only(src: bytes) -> bytes:
+    """C/C++ source without comments, trailing blanks and empty lines, so
+    that an edit to a comment does not change the hash of the code."""
+    import re
+
+    text = re.sub(rb"/\*.*?\*/", b"", src, flags=re.S)
+    text = re.sub(rb"//[^\n]*", b"", text)
+    return b"\n".join(line.rstrip() for line in text.split(b"\n") if line.strip())
+
+
 def _kernel_source_sha() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    # The quantization kernel's sources and its launch planner (plan_quant in
+    # The quantization kernel's code and its launch planner (plan_quant in
     # the ABI file); the other entry points of the library do not enter.
     csrc = os.path.join(ROOT, "mxfp4_activation_amd", "csrc")
     for name in ("wush_kernels.hip", "wush_kernels.h"):
         with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
+            h.update(_code_only(f.read()))
     with open(os.path.join(csrc, "wush_abi.cpp"), "rb") as f:
         abi = f.read()
     start = abi.find(b"void plan_quant(")
-    h.update(abi[start:abi.find(b"\n}\n", start) + 3] if start >= 0 else abi)
+    h.update(_code_only(abi[start:abi.find(b"\n}\n", start) + 3] if start >= 0 else abi))
     return h.hexdigest()[:16]
 
 

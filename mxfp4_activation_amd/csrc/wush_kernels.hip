@@ -20,11 +20,13 @@
 //    plus one exchange between lanes l and l^32.  A 16-group (NVFP4, with a
 //    block-diagonal pair as A) is entirely in-lane.
 //  * Exact scales.  A second MFMA pair bounds sum_j |T_ij||x_j| (MXFP4:
-//    max|T| times the token's L1 norm; INT4 and NVFP4: the exact per-output
-//    sums from |T| x |x|), which bounds how far the fp32 accumulation can
-//    be from the exact sum.  If a group's scale decision is not constant
-//    over [amax - d, amax + d], the wave recomputes that token's panel in
-//    float64.  The result is then the exactly rounded y.
+//    max|T| times the token's L1 norm; INT4 and NVFP4: the per-output sums
+//    from |T| x |x|), which bounds how far the fp32 accumulation can be
+//    from the exact sum.  If a group's scale decision is not constant over
+//    [amax - d, amax + d], the outputs that can hold the group's maximum
+//    are recomputed in float64 and rounded once to fp32, and the scale is
+//    decided again on their maximum, the exactly rounded AbsMax.  The codes
+//    keep the matrix-core values.
 //
 // Memory layout and ABI: see include/wush.h.
 
