@@ -100,6 +100,28 @@ def test_gptq_wush_matches_oracle(fmt, G, mode):
     assert e_got == pytest.approx(e_ref, rel=1e-2)
 
 
+def test_gptq_wush_matches_oracle_wide():
+    """A 1024-wide layer: 32 blocks, a 16 x 16 grid of 64-wide tiles in the
+    Hessian GEMM and the blocked Cholesky, updates of up to 992 columns.
+    Same bar as the small case."""
+    from mxfp4_activation_amd import gptq as pg
+
+    W, Xc, _ = gen_linear_layer(1024, 384, 2048, 1, seed=14, n_outlier=10)
+    ref = gptq.gptq_wush_ref(W, Xc, 32, "mxfp4", gptq=True)
+    got = pg.gptq_wush(torch.from_numpy(W).cuda(), torch.from_numpy(Xc).cuda(), 32, "mxfp4", gptq=True)
+    torch.cuda.synchronize()
+    tx = got.T_x.cpu().numpy()
+    scale = np.abs(ref.T_x).max(axis=(1, 2), keepdims=True)
+    err = (np.abs(tx - ref.T_x) / scale).max()
+    print("T_x max relative difference %.3g" % err, flush=True)
+    assert err < 1e-8
+    lv = lambda c: codecs.e2m1_level_index(codecs.unpack_nibbles(c))
+    d = np.abs(lv(got.codes.cpu().numpy()).astype(int) - lv(ref.codes).astype(int))
+    print("weight codes one level apart: %d of %d" % ((d > 0).sum(), d.size), flush=True)
+    assert d.max() <= 1 and (d > 0).mean() <= 1e-3
+    np.testing.assert_array_equal(got.scales.cpu().numpy(), ref.scales)
+
+
 def test_gptq_wush_cholesky_factor():
     """The library's blocked Cholesky of the damped Hessian against LAPACK's
     on the same float64 Hessian (a library routine on the definition, not
