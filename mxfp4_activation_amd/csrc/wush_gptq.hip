@@ -7,7 +7,8 @@
 //      Cholesky factor (blocked: panel factorization, triangular solve of
 //      the rows below, update of the trailing matrix).
 //   2. Y = W X'.
-//   3. For b = C-1 .. 0, one workgroup (gptq_wush_block_kernel):
+//   3. For b = C-1 .. 0 (gptq_wush_block_kernel; each workgroup of the
+//      launch derives the block's transforms, then takes 256 channels):
 //        the SVD of Y_b = Y[:, b] through its Gram matrix Y_b^T Y_b, whose
 //        eigenvectors V (one-sided Jacobi) and eigenvalues s^2 give
 //        U = Y_b V S^-1; each (u_k, v_k) signed so that v_k's largest entry
@@ -280,8 +281,11 @@ struct BlockLds {
 };
 
 // Block b of Algorithm 1 (see the top of this file).  256 threads: the
-// Jacobi rounds give each of the G/2 column pairs G/2 threads; the channel
-// loop gives each thread output channels t, t + 256, ...
+// Jacobi rounds give each of the G/2 column pairs G/2 threads.  Every
+// workgroup of the launch derives the block's transforms (steps 1-4, the
+// same operations in the same order, so the same values); the channel loop
+// then gives thread t of workgroup w the output channels 256 w + t,
+// 256 (w + gridDim.x) + t, ...  Workgroup 0 stores T_X.
 template <int FMT, int G>
 __global__ __launch_bounds__(256) void gptq_wush_block_kernel(GptqWushArgs a, int b) {
   __shared__ BlockLds<G> L;
@@ -390,7 +394,7 @@ __global__ __launch_bounds__(256) void gptq_wush_block_kernel(GptqWushArgs a, in
     L.T[r][l] = tv;
     L.Mb[r][l] = sq_out * mv;
     L.A[r][l] = hv;  // Hd diag(1 / Sn) Hd^T, factored below
-    a.T_x[(int64_t)b * G * G + e] = tv;
+    if (blockIdx.x == 0) a.T_x[(int64_t)b * G * G + e] = tv;
   }
   __syncthreads();
   if (a.use_gptq) {
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(256) void gptq_wush_block_kernel(GptqWushArgs a, in
   // out; Wsub^T T (Wsub = Q for GPTQ, Wbar for round-to-nearest) goes into
   // Wq's block columns for the update of Y that follows this kernel.
   const int64_t C = a.d_in / G;
-  for (int64_t o = t; o < a.d_out; o += 256) {
+  for (int64_t o = (int64_t)blockIdx.x * 256 + t; o < a.d_out; o += (int64_t)gridDim.x * 256) {
     double y[G], q[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) y[i] = Yb[o * ld + i];
@@ -513,9 +517,14 @@ static hipError_t run_gptq_wush(const GptqWushArgs& a, hipStream_t s) {
   y.alpha = 1.0; y.beta = 0.0;
   gemm_f64(y, s);
   // 3. Blocks in reverse order; each updates the columns of the blocks
-  // still to come: Y[:, < lo] -= (Wsub^T T) X'[lo:lo+G, < lo].
+  // still to come: Y[:, < lo] -= (Wsub^T T) X'[lo:lo+G, < lo].  A block's
+  // output channels are spread over workgroups of 256 (at most 256 of
+  // them); each workgroup first derives the block's transforms itself, the
+  // same float64 operations in the same order, so all hold identical
+  // values, and workgroup 0 stores T_X.
+  const unsigned n_wg = (unsigned)((a.d_out + 255) / 256 < 256 ? (a.d_out + 255) / 256 : 256);
   for (int64_t b = C - 1; b >= 0; --b) {
-    hipLaunchKernelGGL((gptq_wush_block_kernel<FMT, G>), dim3(1), dim3(256), 0, s, a, (int)b);
+    hipLaunchKernelGGL((gptq_wush_block_kernel<FMT, G>), dim3(n_wg), dim3(256), 0, s, a, (int)b);
     const int64_t lo = b * G;
     if (lo == 0) continue;
     GemmF64Args u{};

@@ -14,9 +14,9 @@ order, interleaving the transform construction with GPTQ.
      Wbar (RTN).
 
 Every step runs in the library (wush_gptq_wush): the Hessian, its blocked
-Cholesky factorization and the float64 GEMMs, one workgroup per block for
-the SVD (through the block's Gram matrix), the transforms and the
-intra-block GPTQ, and the dequantized weights.  This module only allocates
+Cholesky factorization and the float64 GEMMs, per block the SVD (through
+the block's Gram matrix), the transforms and the intra-block GPTQ, and the
+dequantized weights.  This module only allocates
 the outputs and passes pointers.  MXFP4 and INT4 are supported; NVFP4
 would need a per-tensor scale for weights that do not exist until the last
 block is done.
