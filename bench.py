@@ -106,6 +106,8 @@ def parse():
                     help="with --gemm-layers: measure the fused projections instead (q|k|v as one 6144 x 4096 "
                          "layer, gate|up as one 24576 x 4096 layer, each with one transform bank built from the "
                          "concatenated weight)")
+    ap.add_argument("--gemm-model", default="qwen3-8b", choices=["qwen3-8b", "qwen3-14b", "llama3.1-70b"],
+                    help="with --gemm-layers: whose linear-layer shapes to measure")
     ap.add_argument("--gemm-tokens", type=int, default=0,
                     help="with --gemm-layers: token batch M (default 1024)")
     ap.add_argument("--layer-loss", action="store_true",
@@ -396,8 +398,9 @@ def compare_transforms(args) -> None:
 
 
 def gemm_layers(args) -> None:
-    """Per-layer forward of Eq. 10 on Qwen3-8B linear-layer shapes at 1024
-    tokens, against the bf16 GEMM (deep dive, section 3.4.7 and the
+    """Per-layer forward of Eq. 10 on the linear-layer shapes of Qwen3-8B
+    (or, with --gemm-model, Qwen3-14B or Llama-3.1-70B) at 1024 tokens,
+    against the bf16 GEMM (deep dive, section 3.4.7 and the
     results: speedup of transform + quantization + FP4 MatMul over BF16,
     with "None" = the FP4 MatMul alone).  Weights are random N(0, 0.02) in
     nn.Linear order, pre-quantized offline with the weight-side transform
@@ -409,7 +412,7 @@ def gemm_layers(args) -> None:
     import torch
 
     from mxfp4_activation_amd import ops, transforms
-    from synthetic.gemm_operands import GEMM_TOKENS, QWEN3_8B_FUSED, QWEN3_8B_LAYERS
+    from synthetic.gemm_operands import GEMM_TOKENS, MODEL_LAYERS, QWEN3_8B_FUSED
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -418,7 +421,9 @@ def gemm_layers(args) -> None:
         raise SystemExit("--gemm-tokens must be positive")
     gen = torch.Generator(device="cpu").manual_seed(2024)
     shapes = {}
-    for name, nk in (QWEN3_8B_FUSED if args.gemm_fused else QWEN3_8B_LAYERS).items():
+    if args.gemm_fused and args.gemm_model != "qwen3-8b":
+        raise SystemExit("--gemm-fused measures the Qwen3-8B projections only")
+    for name, nk in (QWEN3_8B_FUSED if args.gemm_fused else MODEL_LAYERS[args.gemm_model]).items():
         shapes.setdefault(nk, []).append(name)
     rows = []
     for (N, K), names in shapes.items():
@@ -490,7 +495,7 @@ def gemm_layers(args) -> None:
                "bf16_gemm_tflops": round(flop / us["bf16"] / 1e6, 1)}
         rows.append(row)
         print(json.dumps(row), flush=True)
-    what = "fused Qwen3-8B projections" if args.gemm_fused else "Qwen3-8B layer shape"
+    what = "fused Qwen3-8B projections" if args.gemm_fused else "%s layer shape" % args.gemm_model
     print(json.dumps({"comparison": "Eq. 10 forward per %s, %d tokens, bf16 output, hot caches" % (what, M),
                       "variants": {"bf16": "torch.matmul (hipBLASLt)",
                                    "wush_quant_fp4": "wush_quant_mxfp4 (T_wush) + wush_gemm_mxfp4",

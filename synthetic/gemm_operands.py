@@ -23,6 +23,36 @@ QWEN3_8B_LAYERS: Dict[str, Tuple[int, int]] = {
     "down_proj": (4096, 12288),
 }
 
+# The other two models of the pages' per-layer speedup comparison (deep
+# dive, section 5), from their published architecture sizes.
+# Qwen3-14B: hidden size 5120, 40 query and 8 key/value heads of width 128,
+# MLP width 17408.
+QWEN3_14B_LAYERS: Dict[str, Tuple[int, int]] = {
+    "q_proj": (5120, 5120),
+    "k_proj": (1024, 5120),
+    "v_proj": (1024, 5120),
+    "o_proj": (5120, 5120),
+    "gate_proj": (17408, 5120),
+    "up_proj": (17408, 5120),
+    "down_proj": (5120, 17408),
+}
+# Llama-3.1-70B: hidden size 8192, 64 query and 8 key/value heads of width
+# 128, MLP width 28672.
+LLAMA31_70B_LAYERS: Dict[str, Tuple[int, int]] = {
+    "q_proj": (8192, 8192),
+    "k_proj": (1024, 8192),
+    "v_proj": (1024, 8192),
+    "o_proj": (8192, 8192),
+    "gate_proj": (28672, 8192),
+    "up_proj": (28672, 8192),
+    "down_proj": (8192, 28672),
+}
+MODEL_LAYERS: Dict[str, Dict[str, Tuple[int, int]]] = {
+    "qwen3-8b": QWEN3_8B_LAYERS,
+    "qwen3-14b": QWEN3_14B_LAYERS,
+    "llama3.1-70b": LLAMA31_70B_LAYERS,
+}
+
 # Projections that share their input, run as one linear layer with the
 # concatenated weight (one transform bank built from that weight): q|k|v and
 # gate|up.

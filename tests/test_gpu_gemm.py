@@ -23,7 +23,7 @@ import pytest
 from oracle import codecs, gemm, quant
 from oracle import transform as tr
 from synthetic import CONFIGS, f64_to_bf16_bits, gen_calibration, gen_weight, gen_x_rows
-from synthetic.gemm_operands import GEMM_TOKENS, QWEN3_8B_LAYERS, gen_mx_operand
+from synthetic.gemm_operands import GEMM_TOKENS, MODEL_LAYERS, QWEN3_8B_LAYERS, gen_mx_operand
 
 pytestmark = pytest.mark.gpu
 
@@ -121,6 +121,30 @@ def test_qwen3_8b_layer_shapes_whole(layer):
     absref = gemm.gemm_mxfp4_abs_ref(ac, asc, bc, bsc)
     ratio = _check_tol(got, ref, absref, K, False)
     print(f"{layer}: {M} x {N} x {K}, every entry, max err / bound = {ratio:.3g}")
+
+
+@pytest.mark.parametrize("model,layer,whole", [("qwen3-14b", "q_proj", True), ("qwen3-14b", "down_proj", True),
+                                               ("llama3.1-70b", "gate_proj", False),
+                                               ("llama3.1-70b", "down_proj", False)])
+def test_other_model_layer_shapes(model, layer, whole):
+    """The Qwen3-14B and Llama-3.1-70B shapes of the per-layer comparison at
+    1024 tokens: every entry where the oracle's float64 product takes
+    seconds, else a grid of sampled rows and columns with every tile edge."""
+    N, K = MODEL_LAYERS[model][layer]
+    M = GEMM_TOKENS
+    ac, asc = gen_mx_operand(M, K, seed=41, scale_lo=112, scale_hi=124)
+    bc, bsc = gen_mx_operand(N, K, seed=42, scale_lo=116, scale_hi=122)
+    got = _gemm(ac, asc, bc, bsc, torch.float32)
+    if whole:
+        rows, cols = np.arange(M), np.arange(N)
+    else:
+        rng = np.random.default_rng(1)
+        rows = np.unique(np.r_[0, 127, 128, M - 1, rng.choice(M, 24, replace=False)])
+        cols = np.unique(np.r_[0, 127, 128, N - 1, rng.choice(N, 24, replace=False)])
+    ref = gemm.gemm_mxfp4_ref(ac[rows], asc[rows], bc[cols], bsc[cols])
+    absref = gemm.gemm_mxfp4_abs_ref(ac[rows], asc[rows], bc[cols], bsc[cols])
+    ratio = _check_tol(got[np.ix_(rows, cols)], ref, absref, K, False)
+    print(f"{model} {layer}: {M} x {N} x {K}, {ref.size} entries, max err / bound = {ratio:.3g}")
 
 
 @pytest.mark.parametrize("layer", ["q_proj", "k_proj"])
