@@ -329,6 +329,7 @@ wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const voi
   g.M = M;
   g.N = N;
   g.K = K;
+  g.ldc = N;
   hipError_t e = wush::launch_gemm_mxfp4(g, out_type == WUSH_OUT_BF16, stream);
   if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
   return WUSH_OK;

@@ -14,8 +14,9 @@ struct GemmArgs {
   const uint8_t* a_scales;  // [M][K/32] E8M0
   const uint8_t* b_codes;   // [N][K/2]
   const uint8_t* b_scales;  // [N][K/32]
-  void* C;                  // [M][N] fp32 or bf16
+  void* C;                  // [M][ldc] fp32 or bf16; columns 0..N-1 written
   int64_t M, N, K;          // K % 256 == 0
+  int64_t ldc;              // row stride of C in elements, >= N
 };
 
 hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, hipStream_t s);

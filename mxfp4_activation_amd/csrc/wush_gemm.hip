@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   const int gw = wave & 3;        // wave within the group
   const int wm = gw >> 1, wn = gw & 1;
   const int64_t m0 = (int64_t)blockIdx.y * BT, n0 = (int64_t)blockIdx.x * BT;
-  const int64_t K = g.K, M = g.M, N = g.N;
+  const int64_t K = g.K, M = g.M, N = g.N, ldc = g.ldc;
   const int64_t row_bytes = K / 2, row_scales = K / 32;
   const int nk = (int)(K / 256);
 
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   // edge, or rows that are not 16-byte aligned, store element by element.
   constexpr int kVec = BF16_OUT ? 8 : 4;
   constexpr int kVecPerRow = BT / kVec;
-  const bool full = m0 + BT <= M && n0 + BT <= N && (N % kVec) == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15) == 0;
+  const bool full = m0 + BT <= M && n0 + BT <= N && (ldc % kVec) == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15) == 0;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   for (int v = tid; v < BT * kVecPerRow; v += kThreads) {
@@ -342,17 +342,17 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
           const f32x2 pr = {src[2 * e], src[2 * e + 1]};
           o[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
         }
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + grow * N + gcol));
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + grow * ldc + gcol));
       } else {
         const f32x4 o = {src[0], src[1], src[2], src[3]};
-        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.C) + grow * N + gcol));
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.C) + grow * ldc + gcol));
       }
     } else if (grow < M) {
       for (int e = 0; e < kVec && gcol + e < N; ++e) {
         if (BF16_OUT)
-          reinterpret_cast<uint16_t*>(g.C)[grow * N + gcol + e] = (uint16_t)f32_to_bf16_rne(src[e]);
+          reinterpret_cast<uint16_t*>(g.C)[grow * ldc + gcol + e] = (uint16_t)f32_to_bf16_rne(src[e]);
         else
-          reinterpret_cast<float*>(g.C)[grow * N + gcol + e] = src[e];
+          reinterpret_cast<float*>(g.C)[grow * ldc + gcol + e] = src[e];
       }
     }
   }
@@ -360,19 +360,46 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
 
 }  // namespace
 
-hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, hipStream_t s) {
-  // 128 x 128 tiles unless that leaves more than a quarter of the 256 CUs
-  // without a tile; then 64 x 64.
-  const int64_t tiles128 = ((g.N + 127) / 128) * ((g.M + 127) / 128);
-  const int bt = tiles128 >= 192 ? 128 : 64;
+template <int TM>
+static void launch_tiles(const GemmArgs& g, bool bf16_out, hipStream_t s) {
+  constexpr int bt = 64 * TM;
   const dim3 grid((unsigned)((g.N + bt - 1) / bt), (unsigned)((g.M + bt - 1) / bt)), block(kThreads);
-  if (bt == 128) {
-    if (bf16_out) hipLaunchKernelGGL((gemm_mxfp4_kernel<2, true>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((gemm_mxfp4_kernel<2, false>), grid, block, 0, s, g);
-  } else {
-    if (bf16_out) hipLaunchKernelGGL((gemm_mxfp4_kernel<1, true>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((gemm_mxfp4_kernel<1, false>), grid, block, 0, s, g);
+  if (bf16_out) hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, true>), grid, block, 0, s, g);
+  else hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, false>), grid, block, 0, s, g);
+}
+
+hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, hipStream_t s) {
+  // One workgroup per CU (by LDS), 256 CUs.  128 x 128 tiles unless that
+  // leaves more than a quarter of the CUs without a tile; then 64 x 64.
+  const int64_t mt = (g.M + 127) / 128, nt = (g.N + 127) / 128;
+  const int64_t tiles128 = mt * nt;
+  if (tiles128 < 192) {
+    launch_tiles<1>(g, bf16_out, s);
+    return hipGetLastError();
   }
+  // A last wave of 128 x 128 tiles that would occupy a quarter of the CUs
+  // or fewer (Qwen3-14B's 5120-wide outputs: 320 tiles) runs as 64 x 64
+  // tiles instead, four times as many, which fill that wave at about half
+  // the time of a 128 x 128 wave: the columns of the whole waves go to one
+  // launch, the remaining columns to a second on the same stream.
+  const int64_t waves = tiles128 / 256, tail = tiles128 % 256;
+  if (tail > 0 && 4 * tail <= 256 && (256 * waves) % mt == 0) {
+    const int64_t n1 = (256 * waves / mt) * 128;
+    if (n1 > 0 && n1 < g.N) {
+      GemmArgs g1 = g, g2 = g;
+      g1.N = n1;
+      g2.N = g.N - n1;
+      g2.b_codes = g.b_codes + n1 * (g.K / 2);
+      g2.b_scales = g.b_scales + n1 * (g.K / 32);
+      g2.C = static_cast<uint8_t*>(g.C) + n1 * (bf16_out ? 2 : 4);
+      launch_tiles<2>(g1, bf16_out, s);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      launch_tiles<1>(g2, bf16_out, s);
+      return hipGetLastError();
+    }
+  }
+  launch_tiles<2>(g, bf16_out, s);
   return hipGetLastError();
 }
 

@@ -81,6 +81,7 @@ _EXACT = [
     (1000, 3000, 2304, 127, 127),  # 128 x 128, 9 steps of 256: the ring wraps mid-way
     (77, 390, 4352, 127, 127),     # 64 x 64, 17 steps
     (64, 64, 2048, 126, 128),      # 64 x 64, 8 steps: one full turn of its ring
+    (1000, 5096, 512, 126, 128),   # 320 tiles of 128: 4096 columns as 128 x 128, the last 1000 as 64 x 64
 ]
 
 
