@@ -100,6 +100,37 @@ def test_gptq_wush_matches_oracle(fmt, G, mode):
     assert e_got == pytest.approx(e_ref, rel=1e-2)
 
 
+@pytest.mark.parametrize("fmt,G,d_in,d_out", [("mxfp4", 32, 128, 600), ("int4", 16, 96, 600),
+                                               ("int4", 32, 64, 65600)])
+def test_gptq_wush_matches_oracle_many_channels(fmt, G, d_in, d_out):
+    """Output channels spread over several workgroups per block (256 each,
+    the last one ragged), and past 256 workgroups (65600 channels: each
+    workgroup loops over several 256-channel groups).  Every workgroup
+    derives the block's transforms itself; all must agree with the oracle.
+    Same bar as the small case, and the scales equal."""
+    from mxfp4_activation_amd import gptq as pg
+
+    print("case", fmt, G, d_in, d_out, flush=True)
+    W, Xc, _ = gen_linear_layer(d_in, d_out, 1024 if d_out < 4096 else 512, 1, seed=15 + d_out, n_outlier=2)
+    ref = gptq.gptq_wush_ref(W, Xc, G, fmt, gptq=True)
+    got = pg.gptq_wush(torch.from_numpy(W).cuda(), torch.from_numpy(Xc).cuda(), G, fmt, gptq=True)
+    torch.cuda.synchronize()
+    tx = got.T_x.cpu().numpy()
+    scale = np.abs(ref.T_x).max(axis=(1, 2), keepdims=True)
+    assert (np.abs(tx - ref.T_x) / scale).max() < 1e-8
+    lv = lambda c: (codecs.int4_decode if fmt == "int4" else codecs.e2m1_level_index)(codecs.unpack_nibbles(c))
+    d = np.abs(lv(got.codes.cpu().numpy()).astype(int) - lv(ref.codes).astype(int))
+    print("weight codes one level apart: %d of %d" % ((d > 0).sum(), d.size), flush=True)
+    assert d.max() <= 1 and (d > 0).mean() <= 1e-3, ((d > 0).mean(), d.max())
+    sg = got.scales.cpu().numpy()
+    sr = ref.scales
+    if fmt == "int4":
+        sg, sr = sg.view(np.uint16), np.asarray(sr).view(np.uint16)
+    mism = (sg != sr).mean()
+    print("scale mismatches: %.3g" % mism, flush=True)
+    assert mism <= 1e-3
+
+
 def test_gptq_wush_matches_oracle_wide():
     """A 1024-wide layer: 32 blocks, a 16 x 16 grid of 64-wide tiles in the
     Hessian GEMM and the blocked Cholesky, updates of up to 992 columns.
