@@ -442,6 +442,9 @@ def gemm_layers(args) -> None:
         Hb = transforms.hadamard_bank(C, G, dev)
         banks = {"wush": (Tw, Tx), "hadamard": (Hb, Hb)}
         wq = {k: ops.quant("mxfp4", Wb, tb[1]) for k, tb in banks.items()}
+        # Weights are quantized offline, and re-laid once (offline too) in
+        # the order the GEMM kernel stages them.
+        wp = {k: ops.gemm_pack_b(*wq[k]) for k in wq}
         xc = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
         xs = torch.empty((M, K // G), dtype=torch.uint8, device=dev)
         Cout = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -453,14 +456,17 @@ def gemm_layers(args) -> None:
         def v_q(k):
             def f():
                 ops.quant("mxfp4", X, banks[k][0], codes=xc, scales=xs)
-                ops.gemm_mxfp4(xc, xs, wq[k][0], wq[k][1], out_dtype=torch.bfloat16, out=Cout)
+                ops.gemm_mxfp4_packed(xc, xs, wp[k], out_dtype=torch.bfloat16, out=Cout)
             return f
 
         def v_none():
+            ops.gemm_mxfp4_packed(xc, xs, wp["wush"], out_dtype=torch.bfloat16, out=Cout)
+
+        def v_none_rows():
             ops.gemm_mxfp4(xc, xs, wq["wush"][0], wq["wush"][1], out_dtype=torch.bfloat16, out=Cout)
 
         variants = {"bf16": v_bf16, "wush_quant_fp4": v_q("wush"), "h_quant_fp4": v_q("hadamard"),
-                    "none_fp4": v_none}
+                    "none_fp4": v_none, "none_fp4_row_major_b": v_none_rows}
         reps = 40
         cap = torch.cuda.Stream()
         graphs = {}
@@ -498,9 +504,10 @@ def gemm_layers(args) -> None:
     what = "fused Qwen3-8B projections" if args.gemm_fused else "%s layer shape" % args.gemm_model
     print(json.dumps({"comparison": "Eq. 10 forward per %s, %d tokens, bf16 output, hot caches" % (what, M),
                       "variants": {"bf16": "torch.matmul (hipBLASLt)",
-                                   "wush_quant_fp4": "wush_quant_mxfp4 (T_wush) + wush_gemm_mxfp4",
+                                   "wush_quant_fp4": "wush_quant_mxfp4 (T_wush) + wush_gemm_mxfp4_packed",
                                    "h_quant_fp4": "same kernels with the blockwise Hadamard bank",
-                                   "none_fp4": "wush_gemm_mxfp4 alone"},
+                                   "none_fp4": "wush_gemm_mxfp4_packed alone (weights packed offline)",
+                                   "none_fp4_row_major_b": "wush_gemm_mxfp4 alone, weights row-major"},
                       "layers": rows}), flush=True)
 
 

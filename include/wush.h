@@ -139,6 +139,31 @@ wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const voi
                             const void* b_scales, int64_t M, int64_t N, int64_t K, void* C,
                             int out_type, hipStream_t stream);
 
+/* Packed weights for wush_gemm_mxfp4_packed.  The pages pre-quantize the
+ * weights offline (deep dive, section 3.4.6, Eq. 10); this library's GEMM can
+ * also take them re-laid once, offline, in the order its kernel stages them,
+ * so that every weight copy of the GEMM reads whole contiguous blocks.  The
+ * pages define no such layout; it is an interface of this library.
+ *   in:  b_codes u8 [N][K/2] (16-byte aligned), b_scales u8 [N][K/32]
+ *        (8-byte aligned): the wush_quant_mxfp4 layout.
+ *   out: packed_codes, Np * K/2 bytes (16-byte aligned), and packed_scales,
+ *        Np * K/32 bytes (8-byte aligned), with Np = N rounded up to a
+ *        multiple of 128.  Per 128-row tile t and 256-element K step s, in
+ *        order of t then s: 16 KB of codes (row r, 16-byte chunk c at byte
+ *        1024 (r / 8) + 16 (8 (r % 8) + (c ^ ((r / 2) % 8)))) and then, in
+ *        the scale buffer, 1 KB of scales (row r at byte 8 r).  Rows past N
+ *        repeat row N - 1.
+ * K must be a positive multiple of 256; N >= 0 (0 is a no-op).  The outputs
+ * must not overlap the inputs or each other.  Errors as for wush_quant. */
+wush_status wush_gemm_pack_b(const void* b_codes, const void* b_scales, int64_t N, int64_t K,
+                             void* packed_codes, void* packed_scales, hipStream_t stream);
+
+/* wush_gemm_mxfp4 with B in the wush_gemm_pack_b layout (N the unpadded row
+ * count).  Same arguments, requirements and result, bit for bit. */
+wush_status wush_gemm_mxfp4_packed(const void* a_codes, const void* a_scales, const void* b_packed_codes,
+                                   const void* b_packed_scales, int64_t M, int64_t N, int64_t K, void* C,
+                                   int out_type, hipStream_t stream);
+
 /* Dequantization: out[m][k] = the value code k of row m stands for,
  *   MXFP4  e2m1(code) * 2^(scale - 127)                  (G = 32)
  *   NVFP4  e2m1(code) * fp32(E4M3(scale) * g)            (G = 16)

@@ -295,10 +295,9 @@ wush_status wush_nvfp4_global_scale(const void* X, const void* T, int64_t M, int
   return WUSH_OK;
 }
 
-wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const void* b_codes,
-                            const void* b_scales, int64_t M, int64_t N, int64_t K, void* C, int out_type,
-                            hipStream_t stream) {
-  g_last_error[0] = 0;
+static wush_status gemm_common(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
+                               int64_t M, int64_t N, int64_t K, void* C, int out_type, bool packed_b,
+                               hipStream_t stream) {
   if (out_type != WUSH_OUT_F32 && out_type != WUSH_OUT_BF16) return fail(WUSH_EINVAL, "unknown out_type %d", out_type);
   if (M < 0 || N < 0) return fail(WUSH_EINVAL, "M and N must be >= 0");
   if (K <= 0 || K % 256 != 0) return fail(WUSH_EINVAL, "K must be a positive multiple of 256 (got %lld)", (long long)K);
@@ -312,9 +311,11 @@ wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const voi
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16)) return fail(WUSH_EALIGN, "codes must be 16-byte aligned");
   if (!aligned(a_scales, 8) || !aligned(b_scales, 8)) return fail(WUSH_EALIGN, "scales must be 8-byte aligned");
   if (!aligned(C, 4)) return fail(WUSH_EALIGN, "C must be 4-byte aligned");
+  // Packed B covers N rounded up to a multiple of 128 rows.
+  const int64_t nrows_b = packed_b ? (N + 127) / 128 * 128 : N;
   const uint64_t nc = (uint64_t)M * N * (out_type == WUSH_OUT_F32 ? 4 : 2);
-  const uint64_t na = (uint64_t)M * K / 2, nb = (uint64_t)N * K / 2;
-  const uint64_t nsa = (uint64_t)M * K / 32, nsb = (uint64_t)N * K / 32;
+  const uint64_t na = (uint64_t)M * K / 2, nb = (uint64_t)nrows_b * K / 2;
+  const uint64_t nsa = (uint64_t)M * K / 32, nsb = (uint64_t)nrows_b * K / 32;
   if (overlap(C, nc, a_codes, na) || overlap(C, nc, b_codes, nb) || overlap(C, nc, a_scales, nsa) ||
       overlap(C, nc, b_scales, nsb))
     return fail(WUSH_EINVAL, "C overlaps an input");
@@ -330,7 +331,48 @@ wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const voi
   g.N = N;
   g.K = K;
   g.ldc = N;
-  hipError_t e = wush::launch_gemm_mxfp4(g, out_type == WUSH_OUT_BF16, stream);
+  hipError_t e = wush::launch_gemm_mxfp4(g, out_type == WUSH_OUT_BF16, packed_b, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const void* b_codes,
+                            const void* b_scales, int64_t M, int64_t N, int64_t K, void* C, int out_type,
+                            hipStream_t stream) {
+  g_last_error[0] = 0;
+  return gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, C, out_type, false, stream);
+}
+
+wush_status wush_gemm_mxfp4_packed(const void* a_codes, const void* a_scales, const void* b_packed_codes,
+                                   const void* b_packed_scales, int64_t M, int64_t N, int64_t K, void* C,
+                                   int out_type, hipStream_t stream) {
+  g_last_error[0] = 0;
+  return gemm_common(a_codes, a_scales, b_packed_codes, b_packed_scales, M, N, K, C, out_type, true, stream);
+}
+
+wush_status wush_gemm_pack_b(const void* b_codes, const void* b_scales, int64_t N, int64_t K, void* packed_codes,
+                             void* packed_scales, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (N < 0) return fail(WUSH_EINVAL, "N must be >= 0");
+  if (K <= 0 || K % 256 != 0) return fail(WUSH_EINVAL, "K must be a positive multiple of 256 (got %lld)", (long long)K);
+  if (K > ((int64_t)1 << 30)) return fail(WUSH_EINVAL, "K too large");
+  if (N == 0) return WUSH_OK;
+  const int64_t nr = (N + 127) / 128 * 128;
+  if (nr > (INT64_MAX / 8) / K || nr / 128 * (K / 256) * 1024 > 0x7FFFFFFFLL * 256)
+    return fail(WUSH_EINVAL, "sizes overflow");
+  if (!b_codes || !b_scales || !packed_codes || !packed_scales) return fail(WUSH_EINVAL, "null pointer");
+  if (!aligned(b_codes, 16) || !aligned(packed_codes, 16)) return fail(WUSH_EALIGN, "codes must be 16-byte aligned");
+  if (!aligned(b_scales, 8) || !aligned(packed_scales, 8)) return fail(WUSH_EALIGN, "scales must be 8-byte aligned");
+  const uint64_t nb = (uint64_t)N * K / 2, nsb = (uint64_t)N * K / 32;
+  const uint64_t npb = (uint64_t)nr * K / 2, npsb = (uint64_t)nr * K / 32;
+  if (overlap(packed_codes, npb, b_codes, nb) || overlap(packed_codes, npb, b_scales, nsb) ||
+      overlap(packed_scales, npsb, b_codes, nb) || overlap(packed_scales, npsb, b_scales, nsb) ||
+      overlap(packed_codes, npb, packed_scales, npsb))
+    return fail(WUSH_EINVAL, "packed outputs overlap an input or each other");
+  wush_status st = check_device();
+  if (st != WUSH_OK) return st;
+  hipError_t e = wush::launch_pack_b(static_cast<const uint8_t*>(b_codes), static_cast<const uint8_t*>(b_scales), N, K,
+                                     static_cast<uint8_t*>(packed_codes), static_cast<uint8_t*>(packed_scales), stream);
   if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
   return WUSH_OK;
 }

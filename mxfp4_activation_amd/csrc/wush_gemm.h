@@ -19,7 +19,14 @@ struct GemmArgs {
   int64_t ldc;              // row stride of C in elements, >= N
 };
 
-hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, hipStream_t s);
+// packed_b: b_codes / b_scales are in the layout launch_pack_b writes.
+hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, bool packed_b, hipStream_t s);
+
+// B [N][K/2] codes and [N][K/32] scales -> the packed layout: per 128-row tile
+// and 256-element K step, 16 KB of codes and 1 KB of scales in the order the
+// GEMM kernel stages them (rows rounded up to a multiple of 128).
+hipError_t launch_pack_b(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, uint8_t* packed_codes,
+                         uint8_t* packed_scales, hipStream_t s);
 
 }  // namespace wush
 

@@ -50,6 +50,12 @@
 // At the end each K group writes its partial tile into its own fp32 region
 // of LDS; the store pass adds the two and writes C with 16-byte
 // row-contiguous stores.
+//
+// Packed B (PACKED_B): weights re-laid once, offline (pack_b_kernel), as
+// the LDS image of every (128-row tile, K step): the B copies then read
+// 1 KB (codes) and 256 B (scales) contiguously instead of 8 or 32 rows per
+// instruction.  Everything after the copies is the same code, so the
+// result is the same bit for bit.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -67,6 +73,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowB = 128;                // code bytes per row per step (256 elements)
 constexpr int kGroups = 2;
+constexpr int kPackStep = 128 * kRowB;    // packed B: code bytes of one 128-row tile per step
 constexpr int kThreads = 256 * kGroups;
 constexpr int kLdsB = 139264;             // 4 stages of 128-row tiles or 8 of 64-row tiles
 
@@ -130,7 +137,7 @@ __device__ __forceinline__ void dma4(glb_u8* src, uint32_t dst) {
 }
 #pragma clang diagnostic pop
 
-template <int TM, bool BF16_OUT>
+template <int TM, bool BF16_OUT, bool PACKED_B>
 __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   using Gm = Geo<TM>;
   constexpr int BT = Gm::BT;
@@ -151,6 +158,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   // Load map.  Code loads: wave w moves rows 8 (TM w + q) .. +7 (q < TM) of
   // both tiles; lane L takes row L / 8 of those 8 and stores LDS slot L % 8,
   // which holds chunk (L % 8) ^ ((row / 2) % 8).
+  // Packed B: 128-row tiles, each step kPackStep code bytes and 1 KB of
+  // scales; a 64-row tile (TM = 1) is the second half of its 128-row tile
+  // when n0 % 128 == 64.
+  const int64_t pt_rows = (n0 / 128) * 128;  // first row of the packed tile
+  const int p_half = (int)((n0 % 128) / 64);
   glb_u8* a_src[TM];
   glb_u8* b_src[TM];
 #pragma unroll
@@ -162,6 +174,10 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
     rb = rb < N ? rb : N - 1;
     a_src[q] = (glb_u8*)g.a_codes + ra * row_bytes + 16 * chunk;
     b_src[q] = (glb_u8*)g.b_codes + rb * row_bytes + 16 * chunk;
+    // Packed B: the tile's step already sits in its LDS image order, so
+    // each copy reads 1 KB contiguously (see pack_b_kernel).
+    if (PACKED_B)
+      b_src[q] = (glb_u8*)g.b_codes + pt_rows * row_bytes + (kPackStep / 2) * p_half + 1024 * (TM * wave + q) + 16 * lane;
   }
   // Scale loads: waves 0..3 move A rows 16 TM w + L / 2, waves 4..7 B rows
   // 16 TM (w - 4) + L / 2, 4 bytes (half a row's 8) per lane; lanes from
@@ -172,6 +188,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   const int64_t s_lim = s_is_a ? M : N;
   s_row = s_row < s_lim ? s_row : s_lim - 1;
   glb_u8* s_src = (glb_u8*)(s_is_a ? g.a_scales : g.b_scales) + s_row * row_scales + 4 * (lane & 1);
+  int64_t s_step = 8;  // scale bytes per step: 8 per row, or a packed tile's 1 KB
+  if (PACKED_B && !s_is_a) {
+    s_src = (glb_u8*)g.b_scales + pt_rows * row_scales + 512 * p_half + 128 * TM * (wave & 3) + 4 * lane;
+    s_step = 8 * 128;
+  }
   const int s_dst = (s_is_a ? Gm::kOffSA : Gm::kOffSB) + 128 * TM * (wave & 3);
 
   // Step ks lives in ring stage ks % kStages.
@@ -182,9 +203,9 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < TM; ++q) {
       dma16(a_src[q] + kc * kRowB, st + 1024 * (TM * wave_u + q));
-      dma16(b_src[q] + kc * kRowB, st + Gm::kOffB + 1024 * (TM * wave_u + q));
+      dma16(b_src[q] + kc * (PACKED_B ? kPackStep : kRowB), st + Gm::kOffB + 1024 * (TM * wave_u + q));
     }
-    if (s_lane) dma4(s_src + kc * 8, st + (uint32_t)__builtin_amdgcn_readfirstlane(s_dst));
+    if (s_lane) dma4(s_src + kc * s_step, st + (uint32_t)__builtin_amdgcn_readfirstlane(s_dst));
   };
 
   f32x16 acc[TM][TM];
@@ -361,27 +382,33 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
 }  // namespace
 
 template <int TM>
-static void launch_tiles(const GemmArgs& g, bool bf16_out, hipStream_t s) {
+static void launch_tiles(const GemmArgs& g, bool bf16_out, bool packed_b, hipStream_t s) {
   constexpr int bt = 64 * TM;
   const dim3 grid((unsigned)((g.N + bt - 1) / bt), (unsigned)((g.M + bt - 1) / bt)), block(kThreads);
-  if (bf16_out) hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, true>), grid, block, 0, s, g);
-  else hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, false>), grid, block, 0, s, g);
+  if (packed_b) {
+    if (bf16_out) hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, true, true>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, false, true>), grid, block, 0, s, g);
+  } else {
+    if (bf16_out) hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, true, false>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, false, false>), grid, block, 0, s, g);
+  }
 }
 
-hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, hipStream_t s) {
+hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, bool packed_b, hipStream_t s) {
   // One workgroup per CU (by LDS), 256 CUs.  128 x 128 tiles unless that
   // leaves more than a quarter of the CUs without a tile; then 64 x 64.
   const int64_t mt = (g.M + 127) / 128, nt = (g.N + 127) / 128;
   const int64_t tiles128 = mt * nt;
   if (tiles128 < 192) {
-    launch_tiles<1>(g, bf16_out, s);
+    launch_tiles<1>(g, bf16_out, packed_b, s);
     return hipGetLastError();
   }
   // A last wave of 128 x 128 tiles that would occupy a quarter of the CUs
   // or fewer (Qwen3-14B's 5120-wide outputs: 320 tiles) runs as 64 x 64
   // tiles instead, four times as many, which fill that wave at about half
   // the time of a 128 x 128 wave: the columns of the whole waves go to one
-  // launch, the remaining columns to a second on the same stream.
+  // launch, the remaining columns to a second on the same stream.  n1 is a
+  // multiple of 128, so B's offset is the same in both layouts.
   const int64_t waves = tiles128 / 256, tail = tiles128 % 256;
   if (tail > 0 && 4 * tail <= 256 && (256 * waves) % mt == 0) {
     const int64_t n1 = (256 * waves / mt) * 128;
@@ -392,14 +419,59 @@ hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, hipStream_t s) {
       g2.b_codes = g.b_codes + n1 * (g.K / 2);
       g2.b_scales = g.b_scales + n1 * (g.K / 32);
       g2.C = static_cast<uint8_t*>(g.C) + n1 * (bf16_out ? 2 : 4);
-      launch_tiles<2>(g1, bf16_out, s);
+      launch_tiles<2>(g1, bf16_out, packed_b, s);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      launch_tiles<1>(g2, bf16_out, s);
+      launch_tiles<1>(g2, bf16_out, packed_b, s);
       return hipGetLastError();
     }
   }
-  launch_tiles<2>(g, bf16_out, s);
+  launch_tiles<2>(g, bf16_out, packed_b, s);
+  return hipGetLastError();
+}
+
+// Packed B.  For each 128-row tile t of B and each K step ks (256
+// elements), 16 KB of codes and 1 KB of scales, laid out exactly as the
+// GEMM kernel stages that step in LDS: byte 1024 i + 16 L of the code
+// block holds 16-byte chunk (L % 8) ^ ((r / 2) % 8) of row r = 8 i + L / 8,
+// and the scale block holds the tile's 128 rows of 8 scale bytes.  Rows
+// past N repeat row N - 1 (the kernel never stores their results).  One
+// thread per 16 code bytes and per 8 scale bytes.
+__global__ __launch_bounds__(256) void pack_b_kernel(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales, int64_t N, int64_t K,
+                                                     uint8_t* __restrict__ pcodes, uint8_t* __restrict__ pscales,
+                                                     int64_t n_code16, int64_t n_scale8) {
+  const int64_t nk = K / 256;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n_code16) {
+    const int64_t tile = i / (nk * 1024), rem = i - tile * nk * 1024;
+    const int64_t ks = rem / 1024;
+    const int o = (int)(rem - ks * 1024), ins = o / 64, L = o % 64;
+    const int r = 8 * ins + L / 8;
+    const int chunk = (L % 8) ^ ((r >> 1) & 7);
+    int64_t row = tile * 128 + r;
+    row = row < N ? row : N - 1;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(codes + row * (K / 2) + ks * kRowB + 16 * chunk);
+    *reinterpret_cast<u32x4*>(pcodes + 16 * i) = v;
+  }
+  if (i < n_scale8) {
+    const int64_t tile = i / (nk * 128), rem = i - tile * nk * 128;
+    const int64_t ks = rem / 128;
+    const int r = (int)(rem - ks * 128);
+    int64_t row = tile * 128 + r;
+    row = row < N ? row : N - 1;
+    const u32x2 v = *reinterpret_cast<const u32x2*>(scales + row * (K / 32) + ks * 8);
+    *reinterpret_cast<u32x2*>(pscales + 8 * i) = v;
+  }
+}
+
+hipError_t launch_pack_b(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, uint8_t* pcodes,
+                         uint8_t* pscales, hipStream_t s) {
+  const int64_t tiles = (N + 127) / 128, nk = K / 256;
+  const int64_t n_code16 = tiles * nk * 1024, n_scale8 = tiles * nk * 128;
+  const int64_t blocks = (n_code16 + 255) / 256;
+  hipLaunchKernelGGL(pack_b_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales, N, K, pcodes, pscales,
+                     n_code16, n_scale8);
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@ library call on torch's current stream.  No arithmetic of the path runs here.
 
 from __future__ import annotations
 
-from typing import Optional, Tuple
+from typing import NamedTuple, Optional, Tuple
 
 import torch
 
@@ -164,6 +164,59 @@ def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Ten
     _lib.check(lib.wush_gemm_mxfp4(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(), b_scales.data_ptr(),
                                    M, N, K, out.data_ptr(), 1 if out_dtype == torch.bfloat16 else 0, _stream()),
                "wush_gemm_mxfp4")
+    return out
+
+
+class PackedB(NamedTuple):
+    """MXFP4 weights in the layout of wush_gemm_pack_b: N rounded up to a
+    multiple of 128 rows, per 128-row tile and 256-element K step the codes
+    and scales in the order the GEMM kernel stages them."""
+    codes: torch.Tensor   # uint8 [Np * K / 2]
+    scales: torch.Tensor  # uint8 [Np * K / 32]
+    N: int
+    K: int
+
+
+def gemm_pack_b(b_codes: torch.Tensor, b_scales: torch.Tensor) -> PackedB:
+    """Re-lay MXFP4 weights (codes [N][K/2], E8M0 scales [N][K/32]) for
+    gemm_mxfp4_packed; done once, offline."""
+    for t in (b_codes, b_scales):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError("codes and scales must be contiguous 2-D uint8 device tensors")
+    N, K = b_codes.shape[0], b_codes.shape[1] * 2
+    if tuple(b_scales.shape) != (N, K // 32):
+        raise ValueError("operand shapes do not match")
+    Np = (N + 127) // 128 * 128
+    pc = torch.empty(Np * K // 2, dtype=torch.uint8, device=b_codes.device)
+    ps = torch.empty(Np * K // 32, dtype=torch.uint8, device=b_codes.device)
+    lib = _lib.load()
+    _lib.check(lib.wush_gemm_pack_b(b_codes.data_ptr(), b_scales.data_ptr(), N, K, pc.data_ptr(), ps.data_ptr(),
+                                    _stream()), "wush_gemm_pack_b")
+    return PackedB(pc, ps, N, K)
+
+
+def gemm_mxfp4_packed(a_codes: torch.Tensor, a_scales: torch.Tensor, b: PackedB,
+                      out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gemm_mxfp4 with the weights from gemm_pack_b: the same result."""
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    for t in (a_codes, a_scales, b.codes, b.scales):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("codes and scales must be contiguous uint8 device tensors")
+    M, N, K = a_codes.shape[0], b.N, a_codes.shape[1] * 2
+    Np = (N + 127) // 128 * 128
+    if (a_codes.dim() != 2 or b.K != K or tuple(a_scales.shape) != (M, K // 32)
+            or b.codes.numel() != Np * K // 2 or b.scales.numel() != Np * K // 32):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    lib = _lib.load()
+    _lib.check(lib.wush_gemm_mxfp4_packed(a_codes.data_ptr(), a_scales.data_ptr(), b.codes.data_ptr(),
+                                          b.scales.data_ptr(), M, N, K, out.data_ptr(),
+                                          1 if out_dtype == torch.bfloat16 else 0, _stream()),
+               "wush_gemm_mxfp4_packed")
     return out
 
 

@@ -61,7 +61,11 @@ hipError_t launch_absmax(int, const QuantArgs& a, int n_wg, hipStream_t) {
 }
 hipError_t launch_global_scale(float*, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_e2m1(const float*, int64_t, uint8_t*, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_gemm_mxfp4(const GemmArgs&, bool, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_gemm_mxfp4(const GemmArgs&, bool, bool, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_pack_b(const uint8_t*, const uint8_t*, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_dequant(int, const uint8_t*, const void*, const float*, int64_t, int64_t, float*, hipStream_t) {
   ++g_launches;
   return hipSuccess;

@@ -104,6 +104,41 @@ def test_gemm_validation_rejects_bad_arguments():
     assert b"multiple of 256" in lib.wush_last_error()
 
 
+def test_gemm_packed_validation_rejects_bad_arguments():
+    lib = wush.load()
+    B = A * 64
+    g = lambda ac, as_, bc, bs, M, N, K, C, t=0: lib.wush_gemm_mxfp4_packed(ac, as_, bc, bs, M, N, K, C, t, None)
+    args = (A, A * 2, A * 3, A * 4)
+    assert g(*args, 0, 16, 256, B) == _lib.WUSH_OK  # M = 0: no-op
+    assert g(*args, -1, 16, 256, B) == _lib.WUSH_EINVAL
+    assert g(*args, 16, 16, 128, B) == _lib.WUSH_EINVAL  # K not a multiple of 256
+    assert g(*args, 16, 16, 256, B, 2) == _lib.WUSH_EINVAL
+    assert g(A, A * 2, None, A * 4, 16, 16, 256, B) == _lib.WUSH_EINVAL
+    assert g(A, A * 2, A * 3 + 8, A * 4, 16, 16, 256, B) == _lib.WUSH_EALIGN
+    assert g(A, A * 2, A * 3, A * 4 + 4, 16, 16, 256, B) == _lib.WUSH_EALIGN
+    # Packed B covers N rounded up to 128 rows (16 KB of codes at K = 256):
+    # a C placed past N's 2 KB but inside the padding overlaps it.
+    assert g(*args, 16, 16, 256, A * 3 + 4096) == _lib.WUSH_EINVAL
+    assert b"overlaps" in lib.wush_last_error()
+
+
+def test_gemm_pack_b_validation_rejects_bad_arguments():
+    lib = wush.load()
+    p = lambda bc, bs, N, K, pc, ps: lib.wush_gemm_pack_b(bc, bs, N, K, pc, ps, None)
+    B = A * 64
+    assert p(A, A * 2, 0, 256, B, B * 2) == _lib.WUSH_OK  # N = 0: no-op
+    assert p(A, A * 2, -1, 256, B, B * 2) == _lib.WUSH_EINVAL
+    assert p(A, A * 2, 16, 320, B, B * 2) == _lib.WUSH_EINVAL  # K not a multiple of 256
+    assert p(None, A * 2, 16, 256, B, B * 2) == _lib.WUSH_EINVAL
+    assert p(A, A * 2, 16, 256, B, None) == _lib.WUSH_EINVAL
+    assert p(A + 8, A * 2, 16, 256, B, B * 2) == _lib.WUSH_EALIGN
+    assert p(A, A * 2, 16, 256, B + 8, B * 2) == _lib.WUSH_EALIGN
+    assert p(A, A * 2, 16, 256, B, B * 2 + 4) == _lib.WUSH_EALIGN
+    assert p(A, A * 2, 16, 256, A + 1024, B * 2) == _lib.WUSH_EINVAL  # packed codes overlap the codes
+    assert p(A, A * 2, 16, 256, B, B + 8192) == _lib.WUSH_EINVAL  # packed scales inside packed codes
+    assert b"overlap" in lib.wush_last_error()
+
+
 def test_dequant_validation_rejects_bad_arguments():
     lib = wush.load()
     B = A * 64

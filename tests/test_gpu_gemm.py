@@ -166,6 +166,62 @@ def test_qwen3_8b_layer_shapes_8192_tokens_sampled(layer):
     _check_tol(got[np.ix_(rows, cols)], ref, absref, K, False)
 
 
+def _packed_layout_ref(bc, bs):
+    """The wush_gemm_pack_b layout as include/wush.h states it, in NumPy."""
+    N, K = bc.shape[0], bc.shape[1] * 2
+    Np, nk = (N + 127) // 128 * 128, K // 256
+    rows = np.minimum(np.arange(Np), N - 1)
+    c = bc[rows].reshape(Np // 128, 128, nk, 8, 16)       # tile, r, step, chunk, byte
+    r = np.arange(128)
+    pc = np.empty((Np // 128, nk, 128, 8, 16), np.uint8)  # tile, step, r, slot, byte
+    for slot in range(8):
+        chunk = slot ^ ((r // 2) % 8)
+        # c[:, r, :, chunk, :] puts the (r, chunk) index first: [r][tile][step][byte]
+        pc[:, :, :, slot, :] = c[:, r, :, chunk, :].transpose(1, 2, 0, 3)
+    s = bs[rows].reshape(Np // 128, 128, nk, 8).transpose(0, 2, 1, 3)
+    return pc.reshape(-1), np.ascontiguousarray(s).reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(128, 256), (200, 512), (1, 768)])
+def test_pack_b_layout(N, K):
+    """The packing kernel writes the layout the header documents (rows past
+    N repeat row N - 1)."""
+    from mxfp4_activation_amd import ops
+
+    bc, bs = gen_mx_operand(N, K, seed=60 + N, scale_lo=110, scale_hi=140)
+    pb = ops.gemm_pack_b(_dev(bc), _dev(bs))
+    torch.cuda.synchronize()
+    ec, es = _packed_layout_ref(bc, bs)
+    np.testing.assert_array_equal(pb.codes.cpu().numpy(), ec)
+    np.testing.assert_array_equal(pb.scales.cpu().numpy(), es)
+
+
+@pytest.mark.parametrize("M,N,K", [(7, 33, 256), (64, 200, 512), (77, 390, 4352), (1000, 3000, 2304),
+                                   (1000, 5096, 512), (1024, 1024, 4096), (1024, 4096, 4096)])
+def test_packed_b_matches_unpacked(M, N, K):
+    """The GEMM with packed weights gives the unpacked GEMM's result bit for
+    bit: 64 x 64 tiles that are second halves of packed 128-row tiles, ragged
+    edges, the split last wave, and whole layer shapes."""
+    from mxfp4_activation_amd import ops
+
+    print("packed", M, N, K, flush=True)
+    ac, asc = gen_mx_operand(M, K, seed=70 + M, scale_lo=105, scale_hi=140)
+    bc, bsc = gen_mx_operand(N, K, seed=71 + N, scale_lo=110, scale_hi=135)
+    a, a_s, b, b_s = _dev(ac), _dev(asc), _dev(bc), _dev(bsc)
+    c1 = ops.gemm_mxfp4(a, a_s, b, b_s, out_dtype=torch.float32)
+    pb = ops.gemm_pack_b(b, b_s)
+    c2 = ops.gemm_mxfp4_packed(a, a_s, pb, out_dtype=torch.float32)
+    c3 = ops.gemm_mxfp4_packed(a, a_s, pb, out_dtype=torch.bfloat16)
+    c4 = ops.gemm_mxfp4(a, a_s, b, b_s, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
+    assert torch.equal(c3.view(torch.int16), c4.view(torch.int16))
+    if M * N * K <= 1 << 31:
+        ref = gemm.gemm_mxfp4_ref(ac, asc, bc, bsc)
+        absref = gemm.gemm_mxfp4_abs_ref(ac, asc, bc, bsc)
+        _check_tol(c2.cpu().numpy(), ref, absref, K, False)
+
+
 @pytest.mark.parametrize("M,N,K", [(64, 64, 2048), (64, 64, 4096), (2048, 2048, 2048), (1024, 4096, 4096)])
 def test_fresh_operands_every_call(M, N, K):
     """Several calls in a row, each with new A operands.  A load that has not
