@@ -447,6 +447,9 @@ def gemm_layers(args) -> None:
         wp = {k: ops.gemm_pack_b(*wq[k]) for k in wq}
         xc = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
         xs = torch.empty((M, K // G), dtype=torch.uint8, device=dev)
+        # The activations' codes and scales in the GEMM's packed layout,
+        # written there by the quantizer itself.
+        xp = ops.quant_mxfp4_packed(X, banks["wush"][0])
         Cout = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         Wt = Wb.t()
 
@@ -455,18 +458,22 @@ def gemm_layers(args) -> None:
 
         def v_q(k):
             def f():
-                ops.quant("mxfp4", X, banks[k][0], codes=xc, scales=xs)
-                ops.gemm_mxfp4_packed(xc, xs, wp[k], out_dtype=torch.bfloat16, out=Cout)
+                ops.quant_mxfp4_packed(X, banks[k][0], out=xp)
+                ops.gemm_mxfp4_packed(xp, wp[k], out_dtype=torch.bfloat16, out=Cout)
             return f
 
         def v_none():
-            ops.gemm_mxfp4_packed(xc, xs, wp["wush"], out_dtype=torch.bfloat16, out=Cout)
+            ops.gemm_mxfp4_packed(xp, wp["wush"], out_dtype=torch.bfloat16, out=Cout)
+
+        def v_q_rows():
+            ops.quant("mxfp4", X, banks["wush"][0], codes=xc, scales=xs)
+            ops.gemm_mxfp4(xc, xs, wq["wush"][0], wq["wush"][1], out_dtype=torch.bfloat16, out=Cout)
 
         def v_none_rows():
             ops.gemm_mxfp4(xc, xs, wq["wush"][0], wq["wush"][1], out_dtype=torch.bfloat16, out=Cout)
 
         variants = {"bf16": v_bf16, "wush_quant_fp4": v_q("wush"), "h_quant_fp4": v_q("hadamard"),
-                    "none_fp4": v_none, "none_fp4_row_major_b": v_none_rows}
+                    "none_fp4": v_none, "wush_quant_fp4_row_major": v_q_rows, "none_fp4_row_major": v_none_rows}
         reps = 40
         cap = torch.cuda.Stream()
         graphs = {}
@@ -504,10 +511,14 @@ def gemm_layers(args) -> None:
     what = "fused Qwen3-8B projections" if args.gemm_fused else "%s layer shape" % args.gemm_model
     print(json.dumps({"comparison": "Eq. 10 forward per %s, %d tokens, bf16 output, hot caches" % (what, M),
                       "variants": {"bf16": "torch.matmul (hipBLASLt)",
-                                   "wush_quant_fp4": "wush_quant_mxfp4 (T_wush) + wush_gemm_mxfp4_packed",
+                                   "wush_quant_fp4": "wush_quant_mxfp4_packed (T_wush) + wush_gemm_mxfp4_packed: "
+                                                     "activations quantized into the GEMM's operand layout, weights "
+                                                     "packed offline",
                                    "h_quant_fp4": "same kernels with the blockwise Hadamard bank",
-                                   "none_fp4": "wush_gemm_mxfp4_packed alone (weights packed offline)",
-                                   "none_fp4_row_major_b": "wush_gemm_mxfp4 alone, weights row-major"},
+                                   "none_fp4": "wush_gemm_mxfp4_packed alone",
+                                   "wush_quant_fp4_row_major": "wush_quant_mxfp4 + wush_gemm_mxfp4, both operands "
+                                                               "row-major",
+                                   "none_fp4_row_major": "wush_gemm_mxfp4 alone, both operands row-major"},
                       "layers": rows}), flush=True)
 
 

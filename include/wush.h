@@ -84,6 +84,20 @@ typedef enum wush_status {
 wush_status wush_quant_mxfp4(const void* X, const void* T, int64_t M, int64_t K,
                              void* codes, void* scales, hipStream_t stream);
 
+/* wush_quant_mxfp4 with its codes and scales written in the packed operand
+ * layout of wush_gemm_mxfp4_packed (the layout wush_gemm_pack_b describes,
+ * over M rows): per 128-row tile and 256-element K step, 16 KB of codes and
+ * 1 KB of scales in the order the GEMM kernel stages them.  The same codes
+ * and scales, bit for bit, only placed differently; each workgroup's 32 rows
+ * become 4 KB and 256 B of contiguous memory.  Rows past M in the last tile
+ * are not written (the GEMM computes them but never stores them).  An
+ * interface of this library: the pages leave the layout open.
+ * K must be a multiple of 256.  packed_codes: Mp * K/2 bytes, 16-byte
+ * aligned; packed_scales: Mp * K/32 bytes, 8-byte aligned; Mp = M rounded up
+ * to a multiple of 128. */
+wush_status wush_quant_mxfp4_packed(const void* X, const void* T, int64_t M, int64_t K,
+                                    void* packed_codes, void* packed_scales, hipStream_t stream);
+
 /* NVFP4 (G = 16).  E2M1 codes.  One OCP E4M3FN scale byte per 16, relative to
  * a per-tensor fp32 scale g read from device memory at `global_scale`:
  *   code = E4M3_rne_sat(fp32(fp32(amax/6) / g)),  eff = E4M3(code) * g,
@@ -159,10 +173,13 @@ wush_status wush_gemm_pack_b(const void* b_codes, const void* b_scales, int64_t 
                              void* packed_codes, void* packed_scales, hipStream_t stream);
 
 /* wush_gemm_mxfp4 with B in the wush_gemm_pack_b layout (N the unpadded row
- * count).  Same arguments, requirements and result, bit for bit. */
-wush_status wush_gemm_mxfp4_packed(const void* a_codes, const void* a_scales, const void* b_packed_codes,
-                                   const void* b_packed_scales, int64_t M, int64_t N, int64_t K, void* C,
-                                   int out_type, hipStream_t stream);
+ * count).  a_packed = 0: A as wush_quant_mxfp4 writes it; a_packed = 1: A in
+ * the same packed layout over M rows, as wush_quant_mxfp4_packed writes it
+ * (buffers of Mp * K/2 and Mp * K/32 bytes, Mp = M rounded up to 128).
+ * Otherwise the same arguments, requirements and result, bit for bit. */
+wush_status wush_gemm_mxfp4_packed(const void* a_codes, const void* a_scales, int a_packed,
+                                   const void* b_packed_codes, const void* b_packed_scales, int64_t M, int64_t N,
+                                   int64_t K, void* C, int out_type, hipStream_t stream);
 
 /* Dequantization: out[m][k] = the value code k of row m stands for,
  *   MXFP4  e2m1(code) * 2^(scale - 127)                  (G = 32)

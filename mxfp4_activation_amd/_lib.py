@@ -23,7 +23,8 @@ SIGNATURES = {
     "wush_quant_int4": (_c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "wush_quant": (_c_int, [_c_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "wush_gemm_mxfp4": (_c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _c_int, _vp]),
-    "wush_gemm_mxfp4_packed": (_c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _c_int, _vp]),
+    "wush_gemm_mxfp4_packed": (_c_int, [_vp, _vp, _c_int, _vp, _vp, _i64, _i64, _i64, _vp, _c_int, _vp]),
+    "wush_quant_mxfp4_packed": (_c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "wush_gemm_pack_b": (_c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "wush_dequant": (_c_int, [_c_int, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
     "wush_gptq_block": (_c_int, [_c_int, _vp, _vp, _c_int, _i64, _vp, _vp, _i64, _vp, _i64, _vp]),

@@ -203,6 +203,38 @@ wush_status wush_quant_mxfp4(const void* X, const void* T, int64_t M, int64_t K,
   return wush_quant(wush::kMXFP4, X, T, M, K, nullptr, codes, scales, nullptr, stream);
 }
 
+wush_status wush_quant_mxfp4_packed(const void* X, const void* T, int64_t M, int64_t K, void* packed_codes,
+                                    void* packed_scales, hipStream_t stream) {
+  g_last_error[0] = 0;
+  wush_status st = check_shape(X, T, M, K, 32);
+  if (st != WUSH_OK || M == 0) return st;
+  if (K % 256 != 0) return fail(WUSH_EINVAL, "K must be a multiple of 256 for the packed layout (got %lld)", (long long)K);
+  if (!packed_codes || !packed_scales) return fail(WUSH_EINVAL, "null codes or scales");
+  if (!aligned(packed_codes, 16)) return fail(WUSH_EALIGN, "codes must be 16-byte aligned");
+  if (!aligned(packed_scales, 8)) return fail(WUSH_EALIGN, "scales must be 8-byte aligned");
+  const int64_t Mp = (M + 127) / 128 * 128;
+  const uint64_t nx = (uint64_t)M * K * 2, nt = (uint64_t)K * 32 * 2;
+  const uint64_t nc = (uint64_t)Mp * K / 2, ns = (uint64_t)Mp * K / 32;
+  if (overlap(packed_codes, nc, X, nx) || overlap(packed_codes, nc, T, nt) || overlap(packed_scales, ns, X, nx) ||
+      overlap(packed_scales, ns, T, nt) || overlap(packed_codes, nc, packed_scales, ns))
+    return fail(WUSH_EINVAL, "output buffers overlap inputs or each other");
+  st = check_device();
+  if (st != WUSH_OK) return st;
+  wush::QuantArgs a{};
+  a.X = static_cast<const uint16_t*>(X);
+  a.T = static_cast<const uint16_t*>(T);
+  a.codes = static_cast<uint8_t*>(packed_codes);
+  a.scales = static_cast<uint8_t*>(packed_scales);
+  a.M = M;
+  a.K = K;
+  plan_quant(wush::kMXFP4, M, K, a);
+  const int64_t n_wg = (int64_t)a.n_pg * a.n_tg;
+  if (n_wg > 0x7FFFFFFF) return fail(WUSH_EINVAL, "problem too large for one launch");
+  hipError_t e = wush::launch_quant_mxfp4_packed(a, (int)n_wg, stream);
+  if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
 wush_status wush_quant_nvfp4(const void* X, const void* T, int64_t M, int64_t K,
                              const float* global_scale, void* codes, void* scales,
                              hipStream_t stream) {
@@ -296,7 +328,7 @@ wush_status wush_nvfp4_global_scale(const void* X, const void* T, int64_t M, int
 }
 
 static wush_status gemm_common(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
-                               int64_t M, int64_t N, int64_t K, void* C, int out_type, bool packed_b,
+                               int64_t M, int64_t N, int64_t K, void* C, int out_type, int layout,
                                hipStream_t stream) {
   if (out_type != WUSH_OUT_F32 && out_type != WUSH_OUT_BF16) return fail(WUSH_EINVAL, "unknown out_type %d", out_type);
   if (M < 0 || N < 0) return fail(WUSH_EINVAL, "M and N must be >= 0");
@@ -312,10 +344,11 @@ static wush_status gemm_common(const void* a_codes, const void* a_scales, const 
   if (!aligned(a_scales, 8) || !aligned(b_scales, 8)) return fail(WUSH_EALIGN, "scales must be 8-byte aligned");
   if (!aligned(C, 4)) return fail(WUSH_EALIGN, "C must be 4-byte aligned");
   // Packed B covers N rounded up to a multiple of 128 rows.
-  const int64_t nrows_b = packed_b ? (N + 127) / 128 * 128 : N;
+  const int64_t nrows_b = layout != wush::kRowMajor ? (N + 127) / 128 * 128 : N;
+  const int64_t nrows_a = layout == wush::kPackedAB ? (M + 127) / 128 * 128 : M;
   const uint64_t nc = (uint64_t)M * N * (out_type == WUSH_OUT_F32 ? 4 : 2);
-  const uint64_t na = (uint64_t)M * K / 2, nb = (uint64_t)nrows_b * K / 2;
-  const uint64_t nsa = (uint64_t)M * K / 32, nsb = (uint64_t)nrows_b * K / 32;
+  const uint64_t na = (uint64_t)nrows_a * K / 2, nb = (uint64_t)nrows_b * K / 2;
+  const uint64_t nsa = (uint64_t)nrows_a * K / 32, nsb = (uint64_t)nrows_b * K / 32;
   if (overlap(C, nc, a_codes, na) || overlap(C, nc, b_codes, nb) || overlap(C, nc, a_scales, nsa) ||
       overlap(C, nc, b_scales, nsb))
     return fail(WUSH_EINVAL, "C overlaps an input");
@@ -331,7 +364,7 @@ static wush_status gemm_common(const void* a_codes, const void* a_scales, const 
   g.N = N;
   g.K = K;
   g.ldc = N;
-  hipError_t e = wush::launch_gemm_mxfp4(g, out_type == WUSH_OUT_BF16, packed_b, stream);
+  hipError_t e = wush::launch_gemm_mxfp4(g, out_type == WUSH_OUT_BF16, layout, stream);
   if (e != hipSuccess) return fail(WUSH_EHIP, "launch: %s", hipGetErrorString(e));
   return WUSH_OK;
 }
@@ -340,14 +373,16 @@ wush_status wush_gemm_mxfp4(const void* a_codes, const void* a_scales, const voi
                             const void* b_scales, int64_t M, int64_t N, int64_t K, void* C, int out_type,
                             hipStream_t stream) {
   g_last_error[0] = 0;
-  return gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, C, out_type, false, stream);
+  return gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, C, out_type, wush::kRowMajor, stream);
 }
 
-wush_status wush_gemm_mxfp4_packed(const void* a_codes, const void* a_scales, const void* b_packed_codes,
-                                   const void* b_packed_scales, int64_t M, int64_t N, int64_t K, void* C,
-                                   int out_type, hipStream_t stream) {
+wush_status wush_gemm_mxfp4_packed(const void* a_codes, const void* a_scales, int a_packed,
+                                   const void* b_packed_codes, const void* b_packed_scales, int64_t M, int64_t N,
+                                   int64_t K, void* C, int out_type, hipStream_t stream) {
   g_last_error[0] = 0;
-  return gemm_common(a_codes, a_scales, b_packed_codes, b_packed_scales, M, N, K, C, out_type, true, stream);
+  if (a_packed != 0 && a_packed != 1) return fail(WUSH_EINVAL, "a_packed must be 0 or 1 (got %d)", a_packed);
+  return gemm_common(a_codes, a_scales, b_packed_codes, b_packed_scales, M, N, K, C, out_type,
+                     a_packed ? wush::kPackedAB : wush::kPackedB, stream);
 }
 
 wush_status wush_gemm_pack_b(const void* b_codes, const void* b_scales, int64_t N, int64_t K, void* packed_codes,

@@ -19,8 +19,11 @@ struct GemmArgs {
   int64_t ldc;              // row stride of C in elements, >= N
 };
 
-// packed_b: b_codes / b_scales are in the layout launch_pack_b writes.
-hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, bool packed_b, hipStream_t s);
+// Operand layouts: kRowMajor (both [rows][K/2] and [rows][K/32]), kPackedB
+// (B in the launch_pack_b layout), kPackedAB (A as the packed quantizer
+// writes it, too).
+constexpr int kRowMajor = 0, kPackedB = 1, kPackedAB = 2;
+hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, int layout, hipStream_t s);
 
 // B [N][K/2] codes and [N][K/32] scales -> the packed layout: per 128-row tile
 // and 256-element K step, 16 KB of codes and 1 KB of scales in the order the

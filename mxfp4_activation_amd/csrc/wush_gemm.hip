@@ -137,7 +137,7 @@ __device__ __forceinline__ void dma4(glb_u8* src, uint32_t dst) {
 }
 #pragma clang diagnostic pop
 
-template <int TM, bool BF16_OUT, bool PACKED_B>
+template <int TM, bool BF16_OUT, bool PACKED_A, bool PACKED_B>
 __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   using Gm = Geo<TM>;
   constexpr int BT = Gm::BT;
@@ -158,11 +158,13 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   // Load map.  Code loads: wave w moves rows 8 (TM w + q) .. +7 (q < TM) of
   // both tiles; lane L takes row L / 8 of those 8 and stores LDS slot L % 8,
   // which holds chunk (L % 8) ^ ((row / 2) % 8).
-  // Packed B: 128-row tiles, each step kPackStep code bytes and 1 KB of
-  // scales; a 64-row tile (TM = 1) is the second half of its 128-row tile
-  // when n0 % 128 == 64.
-  const int64_t pt_rows = (n0 / 128) * 128;  // first row of the packed tile
+  // Packed operands: 128-row tiles, each step kPackStep code bytes and 1 KB
+  // of scales; a 64-row tile (TM = 1) is the second half of its 128-row
+  // tile when its first row % 128 == 64.
+  const int64_t pt_rows = (n0 / 128) * 128;  // first row of B's packed tile
   const int p_half = (int)((n0 % 128) / 64);
+  const int64_t pa_rows = (m0 / 128) * 128;  // the same for A
+  const int pa_half = (int)((m0 % 128) / 64);
   glb_u8* a_src[TM];
   glb_u8* b_src[TM];
 #pragma unroll
@@ -176,6 +178,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
     b_src[q] = (glb_u8*)g.b_codes + rb * row_bytes + 16 * chunk;
     // Packed B: the tile's step already sits in its LDS image order, so
     // each copy reads 1 KB contiguously (see pack_b_kernel).
+    if (PACKED_A)
+      a_src[q] = (glb_u8*)g.a_codes + pa_rows * row_bytes + (kPackStep / 2) * pa_half + 1024 * (TM * wave + q) + 16 * lane;
     if (PACKED_B)
       b_src[q] = (glb_u8*)g.b_codes + pt_rows * row_bytes + (kPackStep / 2) * p_half + 1024 * (TM * wave + q) + 16 * lane;
   }
@@ -193,6 +197,10 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
     s_src = (glb_u8*)g.b_scales + pt_rows * row_scales + 512 * p_half + 128 * TM * (wave & 3) + 4 * lane;
     s_step = 8 * 128;
   }
+  if (PACKED_A && s_is_a) {
+    s_src = (glb_u8*)g.a_scales + pa_rows * row_scales + 512 * pa_half + 128 * TM * (wave & 3) + 4 * lane;
+    s_step = 8 * 128;
+  }
   const int s_dst = (s_is_a ? Gm::kOffSA : Gm::kOffSB) + 128 * TM * (wave & 3);
 
   // Step ks lives in ring stage ks % kStages.
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
     const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lbase + (ks % Gm::kStages) * Gm::kStageB));
 #pragma unroll
     for (int q = 0; q < TM; ++q) {
-      dma16(a_src[q] + kc * kRowB, st + 1024 * (TM * wave_u + q));
+      dma16(a_src[q] + kc * (PACKED_A ? kPackStep : kRowB), st + 1024 * (TM * wave_u + q));
       dma16(b_src[q] + kc * (PACKED_B ? kPackStep : kRowB), st + Gm::kOffB + 1024 * (TM * wave_u + q));
     }
     if (s_lane) dma4(s_src + kc * s_step, st + (uint32_t)__builtin_amdgcn_readfirstlane(s_dst));
@@ -381,26 +389,28 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
 
 }  // namespace
 
-template <int TM>
-static void launch_tiles(const GemmArgs& g, bool bf16_out, bool packed_b, hipStream_t s) {
+template <int TM, bool BF16_OUT>
+static void launch_tiles_out(const GemmArgs& g, int layout, hipStream_t s) {
   constexpr int bt = 64 * TM;
   const dim3 grid((unsigned)((g.N + bt - 1) / bt), (unsigned)((g.M + bt - 1) / bt)), block(kThreads);
-  if (packed_b) {
-    if (bf16_out) hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, true, true>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, false, true>), grid, block, 0, s, g);
-  } else {
-    if (bf16_out) hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, true, false>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, false, false>), grid, block, 0, s, g);
-  }
+  if (layout == kPackedAB) hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, BF16_OUT, true, true>), grid, block, 0, s, g);
+  else if (layout == kPackedB) hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, BF16_OUT, false, true>), grid, block, 0, s, g);
+  else hipLaunchKernelGGL((gemm_mxfp4_kernel<TM, BF16_OUT, false, false>), grid, block, 0, s, g);
 }
 
-hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, bool packed_b, hipStream_t s) {
+template <int TM>
+static void launch_tiles(const GemmArgs& g, bool bf16_out, int layout, hipStream_t s) {
+  if (bf16_out) launch_tiles_out<TM, true>(g, layout, s);
+  else launch_tiles_out<TM, false>(g, layout, s);
+}
+
+hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, int layout, hipStream_t s) {
   // One workgroup per CU (by LDS), 256 CUs.  128 x 128 tiles unless that
   // leaves more than a quarter of the CUs without a tile; then 64 x 64.
   const int64_t mt = (g.M + 127) / 128, nt = (g.N + 127) / 128;
   const int64_t tiles128 = mt * nt;
   if (tiles128 < 192) {
-    launch_tiles<1>(g, bf16_out, packed_b, s);
+    launch_tiles<1>(g, bf16_out, layout, s);
     return hipGetLastError();
   }
   // A last wave of 128 x 128 tiles that would occupy a quarter of the CUs
@@ -419,14 +429,14 @@ hipError_t launch_gemm_mxfp4(const GemmArgs& g, bool bf16_out, bool packed_b, hi
       g2.b_codes = g.b_codes + n1 * (g.K / 2);
       g2.b_scales = g.b_scales + n1 * (g.K / 32);
       g2.C = static_cast<uint8_t*>(g.C) + n1 * (bf16_out ? 2 : 4);
-      launch_tiles<2>(g1, bf16_out, packed_b, s);
+      launch_tiles<2>(g1, bf16_out, layout, s);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      launch_tiles<1>(g2, bf16_out, packed_b, s);
+      launch_tiles<1>(g2, bf16_out, layout, s);
       return hipGetLastError();
     }
   }
-  launch_tiles<2>(g, bf16_out, packed_b, s);
+  launch_tiles<2>(g, bf16_out, layout, s);
   return hipGetLastError();
 }
 

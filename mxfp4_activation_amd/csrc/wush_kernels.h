@@ -51,6 +51,9 @@ struct TransformArgs {
 };
 
 hipError_t launch_quant(int fmt, const QuantArgs& a, int n_wg, hipStream_t s);
+// MXFP4 with codes and scales in the MXFP4 GEMM's packed operand layout
+// (K a multiple of 256; a.codes / a.scales point at the packed buffers).
+hipError_t launch_quant_mxfp4_packed(const QuantArgs& a, int n_wg, hipStream_t s);
 hipError_t launch_transform(int G, const TransformArgs& a, int n_wg, hipStream_t s);
 // Writes 0 to a.amax_bits, then folds max |T x| over the tensor into it.
 hipError_t launch_absmax(int G, const QuantArgs& a, int n_wg, hipStream_t s);

@@ -828,7 +828,7 @@ __device__ __forceinline__ void amax_run(const QuantArgs& a, QuantLds<TPW>& L, F
 // per-tensor AbsMax pre-pass) and folds it into *a.amax_bits.  Rows past M
 // repeat row M - 1 and channels past K are zero on both sides, so they
 // change no maximum.
-template <int FMT, int TPW, bool FULL, bool AMAX = false>
+template <int FMT, int TPW, bool FULL, bool AMAX = false, bool PACK = false>
 __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, int cg, int tg) {
   constexpr int G = (FMT == kNVFP4) ? 16 : 32;
   const int tid = threadIdx.x;
@@ -924,6 +924,38 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
   const int code_row_bytes = FULL ? kPanels * 16 : (int)(code_bytes_left < kPanels * 16 ? code_bytes_left : kPanels * 16);
   constexpr int kCodeThreads = 32 * kPanels;
   const int c_row = tid / kPanels, c_panel = tid % kPanels;
+  if constexpr (PACK) {
+    // The MXFP4 GEMM's operand layout (wush_quant_mxfp4_packed): per
+    // 128-row tile and 256-element K step (this workgroup's column), 16 KB
+    // of codes in the order the GEMM kernel stages them (row r's 16-byte
+    // chunk c at 1024 (r / 8) + 16 (8 (r % 8) + (c ^ ((r / 2) % 8)))) and
+    // 1 KB of scales (row r at 8 r).  A tile's 32 rows are 4 KB and 256 B
+    // of contiguous whole lines.  K is a multiple of 256 here.
+    const int64_t nk = K / 256, ks = p0 / kPanels;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (!FULL && u >= n_tiles) break;
+      const int64_t m_t = (tile0 + u) * 32;  // first row of the tile
+      const int r0 = (int)(m_t % 128);
+      const uint8_t* xs = L.xs[u];
+      if (tid < kCodeThreads) {
+        const int r = r0 + c_row;
+        if (FULL || m_t + c_row < M) {
+          uint8_t* dst = a.codes + ((m_t / 128) * nk + ks) * 16384 + 1024 * (r >> 3) +
+                         16 * (8 * (r & 7) + (c_panel ^ ((r >> 1) & 7)));
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(xs + c_row * kXRow + 64 * c_panel);
+        }
+      } else if (tid < kCodeThreads + 32) {
+        const int rl = tid - kCodeThreads;
+        if (FULL || m_t + rl < M) {
+          uint8_t* dst = a.scales + ((m_t / 128) * nk + ks) * 1024 + 8 * (r0 + rl);
+          *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const u32x2*>(xs + rl * kXRow + kScaleOff);
+        }
+      }
+    }
+    if (a.n_exact && n_exact && lane == 0) atomicAdd(a.n_exact, n_exact);
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     if (!FULL && u >= n_tiles) break;
@@ -981,14 +1013,14 @@ __device__ __forceinline__ void quant_run(const QuantArgs& a, QuantLds<TPW>& L, 
 // path (quant_run<.., false>) keeps one register in scratch; the full-tile
 // path spills nothing.  Three-tile runs (51 KB) fit three workgroups per CU
 // by their LDS alone, so they ask for 6 waves per SIMD.
-template <int FMT, int TPW>
+template <int FMT, int TPW, bool PACK = false>
 __global__ __launch_bounds__(kQWaves * 64, TPW == 3 ? 6 : 8) void quant_kernel(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) QuantLds<TPW> L;
   int cg, tg;
   wg_coords(a.n_pg, a.n_tg, a.token_major, cg, tg);
   const bool full = ((int64_t)(tg + 1) * TPW * 32 <= a.M) && (a.K % (kPanels * 32) == 0) && a.K <= (1 << 26);
-  if (full) quant_run<FMT, TPW, true>(a, L, cg, tg);
-  else quant_run<FMT, TPW, false>(a, L, cg, tg);
+  if (full) quant_run<FMT, TPW, true, false, PACK>(a, L, cg, tg);
+  else quant_run<FMT, TPW, false, false, PACK>(a, L, cg, tg);
 }
 
 // The tensor AbsMax of the transformed activations (NVFP4's per-tensor
@@ -1068,16 +1100,20 @@ __global__ void e2m1_kernel(const float* __restrict__ v, int64_t n, uint8_t* __r
 
 // ---------------------------------------------------------------- launchers
 
-template <int FMT>
+template <int FMT, bool PACK = false>
 static hipError_t launch_quant_fmt(const QuantArgs& a, int n_wg, hipStream_t s) {
   dim3 grid(n_wg), block(kQWaves * 64);
   switch (a.tiles_per_wave) {
-    case 1: hipLaunchKernelGGL((quant_kernel<FMT, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((quant_kernel<FMT, 2>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((quant_kernel<FMT, 3>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((quant_kernel<FMT, 1, PACK>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((quant_kernel<FMT, 2, PACK>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((quant_kernel<FMT, 3, PACK>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quant_mxfp4_packed(const QuantArgs& a, int n_wg, hipStream_t s) {
+  return launch_quant_fmt<kMXFP4, true>(a, n_wg, s);
 }
 
 hipError_t launch_quant(int fmt, const QuantArgs& a, int n_wg, hipStream_t s) {

@@ -167,17 +167,22 @@ def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Ten
     return out
 
 
-class PackedB(NamedTuple):
-    """MXFP4 weights in the layout of wush_gemm_pack_b: N rounded up to a
-    multiple of 128 rows, per 128-row tile and 256-element K step the codes
-    and scales in the order the GEMM kernel stages them."""
-    codes: torch.Tensor   # uint8 [Np * K / 2]
-    scales: torch.Tensor  # uint8 [Np * K / 32]
-    N: int
+class Packed(NamedTuple):
+    """An MXFP4 GEMM operand in the packed layout (wush_gemm_pack_b,
+    wush_quant_mxfp4_packed): rows rounded up to a multiple of 128; per
+    128-row tile and 256-element K step, the codes and scales in the order
+    the GEMM kernel stages them."""
+    codes: torch.Tensor   # uint8 [rows_p * K / 2]
+    scales: torch.Tensor  # uint8 [rows_p * K / 32]
+    rows: int             # unpadded row count
     K: int
 
 
-def gemm_pack_b(b_codes: torch.Tensor, b_scales: torch.Tensor) -> PackedB:
+def _rows_p(rows: int) -> int:
+    return (rows + 127) // 128 * 128
+
+
+def gemm_pack_b(b_codes: torch.Tensor, b_scales: torch.Tensor) -> Packed:
     """Re-lay MXFP4 weights (codes [N][K/2], E8M0 scales [N][K/32]) for
     gemm_mxfp4_packed; done once, offline."""
     for t in (b_codes, b_scales):
@@ -186,35 +191,67 @@ def gemm_pack_b(b_codes: torch.Tensor, b_scales: torch.Tensor) -> PackedB:
     N, K = b_codes.shape[0], b_codes.shape[1] * 2
     if tuple(b_scales.shape) != (N, K // 32):
         raise ValueError("operand shapes do not match")
-    Np = (N + 127) // 128 * 128
-    pc = torch.empty(Np * K // 2, dtype=torch.uint8, device=b_codes.device)
-    ps = torch.empty(Np * K // 32, dtype=torch.uint8, device=b_codes.device)
+    pc = torch.empty(_rows_p(N) * K // 2, dtype=torch.uint8, device=b_codes.device)
+    ps = torch.empty(_rows_p(N) * K // 32, dtype=torch.uint8, device=b_codes.device)
     lib = _lib.load()
     _lib.check(lib.wush_gemm_pack_b(b_codes.data_ptr(), b_scales.data_ptr(), N, K, pc.data_ptr(), ps.data_ptr(),
                                     _stream()), "wush_gemm_pack_b")
-    return PackedB(pc, ps, N, K)
+    return Packed(pc, ps, N, K)
 
 
-def gemm_mxfp4_packed(a_codes: torch.Tensor, a_scales: torch.Tensor, b: PackedB,
-                      out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """gemm_mxfp4 with the weights from gemm_pack_b: the same result."""
+def quant_mxfp4_packed(X: torch.Tensor, T: torch.Tensor, out: Optional[Packed] = None) -> Packed:
+    """quant_mxfp4 with the codes and scales written in the GEMM's packed
+    operand layout (the same values, placed for gemm_mxfp4_packed)."""
+    M, K = _check_x_t(X, T, 32)
+    if K % 256:
+        raise ValueError("the packed layout needs K to be a multiple of 256")
+    if out is None:
+        out = Packed(torch.empty(_rows_p(M) * K // 2, dtype=torch.uint8, device=X.device),
+                     torch.empty(_rows_p(M) * K // 32, dtype=torch.uint8, device=X.device), M, K)
+    elif (out.rows != M or out.K != K or out.codes.numel() != _rows_p(M) * K // 2
+          or out.scales.numel() != _rows_p(M) * K // 32):
+        raise ValueError("out has the wrong size")
+    for t in (out.codes, out.scales):
+        if t.dtype != torch.uint8 or t.device != X.device or not t.is_contiguous():
+            raise ValueError("out must be contiguous uint8 tensors on X's device")
+    lib = _lib.load()
+    _lib.check(lib.wush_quant_mxfp4_packed(X.data_ptr(), T.data_ptr(), M, K, out.codes.data_ptr(),
+                                           out.scales.data_ptr(), _stream()), "wush_quant_mxfp4_packed")
+    return out
+
+
+def gemm_mxfp4_packed(a, b: Packed, out_dtype: torch.dtype = torch.bfloat16,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gemm_mxfp4 with the weights from gemm_pack_b: the same result.  a is
+    either (codes [M][K/2], scales [M][K/32]) as quant_mxfp4 writes them, or
+    a Packed operand from quant_mxfp4_packed."""
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out_dtype must be float32 or bfloat16")
+    a_packed = isinstance(a, Packed)
+    if a_packed:
+        a_codes, a_scales, M, K = a.codes, a.scales, a.rows, a.K
+        if a_codes.numel() != _rows_p(M) * K // 2 or a_scales.numel() != _rows_p(M) * K // 32:
+            raise ValueError("operand shapes do not match")
+    else:
+        a_codes, a_scales = a
+        if a_codes.dim() != 2:
+            raise ValueError("a_codes must be 2-D")
+        M, K = a_codes.shape[0], a_codes.shape[1] * 2
+        if tuple(a_scales.shape) != (M, K // 32):
+            raise ValueError("operand shapes do not match")
     for t in (a_codes, a_scales, b.codes, b.scales):
         if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("codes and scales must be contiguous uint8 device tensors")
-    M, N, K = a_codes.shape[0], b.N, a_codes.shape[1] * 2
-    Np = (N + 127) // 128 * 128
-    if (a_codes.dim() != 2 or b.K != K or tuple(a_scales.shape) != (M, K // 32)
-            or b.codes.numel() != Np * K // 2 or b.scales.numel() != Np * K // 32):
+    N = b.rows
+    if b.K != K or b.codes.numel() != _rows_p(N) * K // 2 or b.scales.numel() != _rows_p(N) * K // 32:
         raise ValueError("operand shapes do not match")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
     elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
     lib = _lib.load()
-    _lib.check(lib.wush_gemm_mxfp4_packed(a_codes.data_ptr(), a_scales.data_ptr(), b.codes.data_ptr(),
-                                          b.scales.data_ptr(), M, N, K, out.data_ptr(),
+    _lib.check(lib.wush_gemm_mxfp4_packed(a_codes.data_ptr(), a_scales.data_ptr(), 1 if a_packed else 0,
+                                          b.codes.data_ptr(), b.scales.data_ptr(), M, N, K, out.data_ptr(),
                                           1 if out_dtype == torch.bfloat16 else 0, _stream()),
                "wush_gemm_mxfp4_packed")
     return out

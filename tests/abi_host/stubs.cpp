@@ -51,6 +51,13 @@ hipError_t launch_quant(int fmt, const QuantArgs& a, int n_wg, hipStream_t) {
   g_last_quant.n_wg = n_wg;
   return hipSuccess;
 }
+hipError_t launch_quant_mxfp4_packed(const QuantArgs& a, int n_wg, hipStream_t) {
+  ++g_launches;
+  g_last_quant.fmt = 0;
+  g_last_quant.args = a;
+  g_last_quant.n_wg = n_wg;
+  return hipSuccess;
+}
 hipError_t launch_transform(int, const TransformArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_absmax(int, const QuantArgs& a, int n_wg, hipStream_t) {
   ++g_launches;
@@ -61,7 +68,7 @@ hipError_t launch_absmax(int, const QuantArgs& a, int n_wg, hipStream_t) {
 }
 hipError_t launch_global_scale(float*, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_e2m1(const float*, int64_t, uint8_t*, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_gemm_mxfp4(const GemmArgs&, bool, bool, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_gemm_mxfp4(const GemmArgs&, bool, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_pack_b(const uint8_t*, const uint8_t*, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t) {
   ++g_launches;
   return hipSuccess;

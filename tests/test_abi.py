@@ -107,7 +107,8 @@ def test_gemm_validation_rejects_bad_arguments():
 def test_gemm_packed_validation_rejects_bad_arguments():
     lib = wush.load()
     B = A * 64
-    g = lambda ac, as_, bc, bs, M, N, K, C, t=0: lib.wush_gemm_mxfp4_packed(ac, as_, bc, bs, M, N, K, C, t, None)
+    g = lambda ac, as_, bc, bs, M, N, K, C, t=0, ap=0: lib.wush_gemm_mxfp4_packed(ac, as_, ap, bc, bs, M, N, K, C, t,
+                                                                               None)
     args = (A, A * 2, A * 3, A * 4)
     assert g(*args, 0, 16, 256, B) == _lib.WUSH_OK  # M = 0: no-op
     assert g(*args, -1, 16, 256, B) == _lib.WUSH_EINVAL
@@ -120,6 +121,24 @@ def test_gemm_packed_validation_rejects_bad_arguments():
     # a C placed past N's 2 KB but inside the padding overlaps it.
     assert g(*args, 16, 16, 256, A * 3 + 4096) == _lib.WUSH_EINVAL
     assert b"overlaps" in lib.wush_last_error()
+    assert g(*args, 16, 16, 256, B, 0, 2) == _lib.WUSH_EINVAL  # a_packed is 0 or 1
+    # Packed A covers M rounded up to 128 rows as well.
+    assert g(*args, 16, 16, 256, A + 4096, 0, 1) == _lib.WUSH_EINVAL
+
+
+def test_quant_mxfp4_packed_validation_rejects_bad_arguments():
+    lib = wush.load()
+    q = lambda X, T, M, K, c, s: lib.wush_quant_mxfp4_packed(X, T, M, K, c, s, None)
+    B = A * 64
+    assert q(A, A * 2, 0, 256, B, B * 2) == _lib.WUSH_OK  # M = 0: no-op
+    assert q(A, A * 2, 4, 320, B, B * 2) == _lib.WUSH_EINVAL  # K not a multiple of 256
+    assert b"multiple of 256" in lib.wush_last_error()
+    assert q(A, A * 2, 4, 256, None, B * 2) == _lib.WUSH_EINVAL
+    assert q(A, A * 2, 4, 256, B + 8, B * 2) == _lib.WUSH_EALIGN
+    assert q(A, A * 2, 4, 256, B, B * 2 + 4) == _lib.WUSH_EALIGN
+    # M = 4 rows pad to 128: the packed codes span 16 KB, so scales 8 KB in overlap.
+    assert q(A, A * 2, 4, 256, B, B + 8192) == _lib.WUSH_EINVAL
+    assert q(A, A * 2, 4, 256, A + 1024, B * 2) == _lib.WUSH_EINVAL  # codes overlap X
 
 
 def test_gemm_pack_b_validation_rejects_bad_arguments():

@@ -23,6 +23,7 @@ import pytest
 from oracle import codecs, gemm, quant
 from oracle import transform as tr
 from synthetic import CONFIGS, f64_to_bf16_bits, gen_calibration, gen_weight, gen_x_rows
+from tests import cases
 from synthetic.gemm_operands import GEMM_TOKENS, MODEL_LAYERS, QWEN3_8B_LAYERS, gen_mx_operand
 
 pytestmark = pytest.mark.gpu
@@ -210,16 +211,69 @@ def test_packed_b_matches_unpacked(M, N, K):
     a, a_s, b, b_s = _dev(ac), _dev(asc), _dev(bc), _dev(bsc)
     c1 = ops.gemm_mxfp4(a, a_s, b, b_s, out_dtype=torch.float32)
     pb = ops.gemm_pack_b(b, b_s)
-    c2 = ops.gemm_mxfp4_packed(a, a_s, pb, out_dtype=torch.float32)
-    c3 = ops.gemm_mxfp4_packed(a, a_s, pb, out_dtype=torch.bfloat16)
+    c2 = ops.gemm_mxfp4_packed((a, a_s), pb, out_dtype=torch.float32)
+    c3 = ops.gemm_mxfp4_packed((a, a_s), pb, out_dtype=torch.bfloat16)
+    # Both operands packed (A re-laid here by the weight packer, which writes
+    # the same layout the packed quantizer does).
+    pa = ops.gemm_pack_b(a, a_s)
+    c5 = ops.gemm_mxfp4_packed(pa, pb, out_dtype=torch.float32)
     c4 = ops.gemm_mxfp4(a, a_s, b, b_s, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
     assert torch.equal(c3.view(torch.int16), c4.view(torch.int16))
+    assert torch.equal(c1.view(torch.int32), c5.view(torch.int32))
     if M * N * K <= 1 << 31:
         ref = gemm.gemm_mxfp4_ref(ac, asc, bc, bsc)
         absref = gemm.gemm_mxfp4_abs_ref(ac, asc, bc, bsc)
         _check_tol(c2.cpu().numpy(), ref, absref, K, False)
+
+
+@pytest.mark.parametrize("M,K", [(128, 256), (77, 512), (1000, 2304), (1024, 4096), (4096, 4096)])
+def test_quant_mxfp4_packed_layout(M, K):
+    """wush_quant_mxfp4_packed writes the row-major quantizer's codes and
+    scales, bit for bit, in the packed layout (rows past M, which it does
+    not write, are left out of the comparison), and the GEMM on two packed
+    operands gives the row-major GEMM's result."""
+    from mxfp4_activation_amd import ops
+
+    print("packed quant", M, K, flush=True)
+    _, tb = cases.transforms("tiny_mxfp4")
+    reps = K // 256
+    T = _dev(np.tile(tb, (reps, 1, 1)).view(np.int16)).view(torch.bfloat16)
+    rng = np.random.default_rng(M + K)
+    X = _dev(f64_to_bf16_bits(rng.standard_t(3, size=(M, K))).view(np.int16)).view(torch.bfloat16)
+    codes, scales = ops.quant_mxfp4(X, T)
+    pq = ops.quant_mxfp4_packed(X, T)
+    torch.cuda.synchronize()
+    c, sc = codes.cpu().numpy(), scales.cpu().numpy()
+    Mp = (M + 127) // 128 * 128
+    pad_c = np.zeros((Mp, K // 2), np.uint8)
+    pad_s = np.zeros((Mp, K // 32), np.uint8)
+    pad_c[:M], pad_s[:M] = c, sc
+    ec, es = _packed_layout_ref(pad_c, pad_s)
+    gc = pq.codes.cpu().numpy().reshape(Mp // 128, K // 256, 128, 128).copy()
+    gs = pq.scales.cpu().numpy().reshape(Mp // 128, K // 256, 128, 8).copy()
+    ec = ec.reshape(gc.shape).copy()
+    es = es.reshape(gs.shape).copy()
+    # Byte block [t][step][r] is row r's 128 code bytes (chunks permuted
+    # within the row), and [t][step][r] of the scales its 8 scale bytes.
+    # Rows past M: zero on both sides before comparing.
+    for t in range(Mp // 128):
+        dead = t * 128 + np.arange(128) >= M
+        gc[t][:, dead] = 0
+        ec[t][:, dead] = 0
+        gs[t][:, dead] = 0
+        es[t][:, dead] = 0
+    np.testing.assert_array_equal(gc, ec)
+    np.testing.assert_array_equal(gs, es)
+    if K >= 256 and M >= 64:
+        N = 384
+        bc, bsc = gen_mx_operand(N, K, seed=5, scale_lo=110, scale_hi=130)
+        pb = ops.gemm_pack_b(_dev(bc), _dev(bsc))
+        c_row = ops.gemm_mxfp4_packed((codes, scales), pb, out_dtype=torch.float32)
+        c_pk = ops.gemm_mxfp4_packed(pq, pb, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(c_row.view(torch.int32), c_pk.view(torch.int32))
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 64, 2048), (64, 64, 4096), (2048, 2048, 2048), (1024, 4096, 4096)])
