@@ -178,6 +178,43 @@ static void other_entries() {
   REJECT(g(A, 2 * A, 3 * A, 4 * A, INT64_MAX / 2, INT64_MAX / 2, 256, B, 0), WUSH_EINVAL);
   ACCEPT(g(A, 2 * A, 3 * A, 4 * A, 16, 16, 256, B, 1), 1);
 
+  auto gp = [](uintptr_t ac, uintptr_t as, int ap, uintptr_t bc, uintptr_t bs, int64_t M, int64_t N, int64_t K,
+               uintptr_t C, int t) {
+    return wush_gemm_mxfp4_packed(P(ac), P(as), ap, P(bc), P(bs), M, N, K, P(C), t, nullptr);
+  };
+  ACCEPT(gp(A, 2 * A, 1, 3 * A, 4 * A, 0, 16, 256, B, 0), 0);
+  REJECT(gp(A, 2 * A, 2, 3 * A, 4 * A, 16, 16, 256, B, 0), WUSH_EINVAL);
+  REJECT(gp(A, 2 * A, 1, 3 * A, 4 * A, 16, 16, 256, A + 4096, 0), WUSH_EINVAL);  // inside A's padded rows
+  REJECT(gp(A, 2 * A, 0, 3 * A, 4 * A, 16, 16, 256, 3 * A + 4096, 0), WUSH_EINVAL);  // inside B's padded rows
+  REJECT(gp(A, 2 * A, 0, 3 * A + 8, 4 * A, 16, 16, 256, B, 0), WUSH_EALIGN);
+  ACCEPT(gp(A, 2 * A, 0, 3 * A, 4 * A, 16, 16, 256, B, 1), 1);
+  ACCEPT(gp(A, 2 * A, 1, 3 * A, 4 * A, 16, 16, 256, B, 0), 1);
+
+  auto pk = [](uintptr_t bc, uintptr_t bs, int64_t N, int64_t K, uintptr_t pc, uintptr_t ps) {
+    return wush_gemm_pack_b(P(bc), P(bs), N, K, P(pc), P(ps), nullptr);
+  };
+  ACCEPT(pk(A, 2 * A, 0, 256, B, 2 * B), 0);
+  REJECT(pk(A, 2 * A, -1, 256, B, 2 * B), WUSH_EINVAL);
+  REJECT(pk(A, 2 * A, 16, 320, B, 2 * B), WUSH_EINVAL);
+  REJECT(pk(A + 8, 2 * A, 16, 256, B, 2 * B), WUSH_EALIGN);
+  REJECT(pk(A, 2 * A, 16, 256, B, 2 * B + 4), WUSH_EALIGN);
+  REJECT(pk(A, 2 * A, 16, 256, A + 1024, 2 * B), WUSH_EINVAL);
+  REJECT(pk(A, 2 * A, 16, 256, B, B + 8192), WUSH_EINVAL);
+  REJECT(pk(A, 2 * A, INT64_MAX / 4, 256, B, 2 * B), WUSH_EINVAL);
+  ACCEPT(pk(A, 2 * A, 16, 256, B, 2 * B), 1);
+
+  auto qp = [](uintptr_t X, uintptr_t T, int64_t M, int64_t K, uintptr_t c, uintptr_t s) {
+    return wush_quant_mxfp4_packed(P(X), P(T), M, K, P(c), P(s), nullptr);
+  };
+  ACCEPT(qp(A, 2 * A, 0, 256, B, 2 * B), 0);
+  REJECT(qp(A, 2 * A, 4, 320, B, 2 * B), WUSH_EINVAL);
+  REJECT(qp(A, 2 * A, 4, 256, 0, 2 * B), WUSH_EINVAL);
+  REJECT(qp(A, 2 * A, 4, 256, B + 8, 2 * B), WUSH_EALIGN);
+  REJECT(qp(A, 2 * A, 4, 256, B, 2 * B + 4), WUSH_EALIGN);
+  REJECT(qp(A, 2 * A, 4, 256, B, B + 8192), WUSH_EINVAL);
+  REJECT(qp(A, 2 * A, 4, 256, A + 1024, 2 * B), WUSH_EINVAL);
+  ACCEPT(qp(A, 2 * A, 4, 256, B, 2 * B), 1);
+
   auto d = [](int fmt, uintptr_t c, uintptr_t s, uintptr_t gs, int64_t M, int64_t K, uintptr_t o) {
     return wush_dequant(fmt, P(c), P(s), static_cast<const float*>(P(gs)), M, K, static_cast<float*>(P(o)), nullptr);
   };
