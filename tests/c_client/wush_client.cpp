@@ -4,6 +4,10 @@
 // requested format and writes the codes and scales to a file, which the
 // GPU test compares with the oracle.
 //
+// With a "WUSHGEM1" input it runs the whole Eq. 10 forward instead:
+// quantize X into the GEMM's packed operand layout, pack the MXFP4 weights
+// once, multiply, and write C.
+//
 // Input file (little-endian):
 //   char[8] "WUSHCLI1"; int32 fmt (0 MXFP4, 1 NVFP4, 2 INT4); int32 G;
 //   int64 M; int64 K; float g (NVFP4: > 0 a static tensor scale, 0 = compute
@@ -12,6 +16,9 @@
 // Output file:
 //   char[8] "WUSHOUT1"; float g used (NVFP4, else 0);
 //   codes [M][K/2] bytes; scales [M][K/G] x (1 byte, or 2 for INT4).
+// GEMM input: char[8] "WUSHGEM1"; int64 M, N, K; X bf16 bits [M][K];
+//   T bf16 bits [K/32][32][32]; weight codes [N][K/2]; weight E8M0 scales
+//   [N][K/32].  GEMM output: char[8] "WUSHOUTG"; C fp32 [M][N].
 // Exit status 0 on success; 2 on a bad input file; 3 on a library or HIP
 // error (the message goes to stderr).
 
@@ -45,6 +52,68 @@ bool read_into(std::FILE* f, V* p, size_t n) {
 
 }  // namespace
 
+// The Eq. 10 forward: wush_quant_mxfp4_packed, wush_gemm_pack_b,
+// wush_gemm_mxfp4_packed.  `in` is positioned after the magic.
+int run_gemm(std::FILE* in, const char* out_path) {
+  int64_t M = 0, N = 0, K = 0;
+  bool ok = read_into(in, &M, 1) && read_into(in, &N, 1) && read_into(in, &K, 1);
+  ok = ok && M > 0 && N > 0 && K > 0 && K % 256 == 0 && M <= (int64_t)1 << 20 && N <= (int64_t)1 << 20 &&
+       K <= (int64_t)1 << 16;
+  if (!ok) {
+    std::fprintf(stderr, "bad input header\n");
+    std::fclose(in);
+    return 2;
+  }
+  const size_t nx = (size_t)M * K, nt = (size_t)K * 32, nwc = (size_t)N * K / 2, nws = (size_t)N * K / 32;
+  const int64_t Mp = (M + 127) / 128 * 128, Np = (N + 127) / 128 * 128;
+  std::vector<uint16_t> x(nx), t(nt);
+  std::vector<uint8_t> wc(nwc), ws(nws);
+  ok = read_into(in, x.data(), nx) && read_into(in, t.data(), nt) && read_into(in, wc.data(), nwc) &&
+       read_into(in, ws.data(), nws);
+  std::fclose(in);
+  if (!ok) {
+    std::fprintf(stderr, "short input file\n");
+    return 2;
+  }
+  void *dX = nullptr, *dT = nullptr, *dWc = nullptr, *dWs = nullptr, *dAc = nullptr, *dAs = nullptr, *dBc = nullptr,
+       *dBs = nullptr, *dC = nullptr;
+  hipStream_t s = nullptr;
+  std::vector<float> c((size_t)M * N);
+  int rc = 3;
+  if (hip_ok(hipMalloc(&dX, nx * 2), "hipMalloc X") && hip_ok(hipMalloc(&dT, nt * 2), "hipMalloc T") &&
+      hip_ok(hipMalloc(&dWc, nwc), "hipMalloc W codes") && hip_ok(hipMalloc(&dWs, nws), "hipMalloc W scales") &&
+      hip_ok(hipMalloc(&dAc, (size_t)Mp * K / 2), "hipMalloc packed A") &&
+      hip_ok(hipMalloc(&dAs, (size_t)Mp * K / 32), "hipMalloc packed A scales") &&
+      hip_ok(hipMalloc(&dBc, (size_t)Np * K / 2), "hipMalloc packed B") &&
+      hip_ok(hipMalloc(&dBs, (size_t)Np * K / 32), "hipMalloc packed B scales") &&
+      hip_ok(hipMalloc(&dC, c.size() * sizeof(float)), "hipMalloc C") && hip_ok(hipStreamCreate(&s), "hipStreamCreate") &&
+      hip_ok(hipMemcpy(dX, x.data(), nx * 2, hipMemcpyHostToDevice), "copy X") &&
+      hip_ok(hipMemcpy(dT, t.data(), nt * 2, hipMemcpyHostToDevice), "copy T") &&
+      hip_ok(hipMemcpy(dWc, wc.data(), nwc, hipMemcpyHostToDevice), "copy W codes") &&
+      hip_ok(hipMemcpy(dWs, ws.data(), nws, hipMemcpyHostToDevice), "copy W scales") &&
+      wush_ok(wush_gemm_pack_b(dWc, dWs, N, K, dBc, dBs, s), "wush_gemm_pack_b") &&
+      wush_ok(wush_quant_mxfp4_packed(dX, dT, M, K, dAc, dAs, s), "wush_quant_mxfp4_packed") &&
+      wush_ok(wush_gemm_mxfp4_packed(dAc, dAs, 1, dBc, dBs, M, N, K, dC, WUSH_OUT_F32, s), "wush_gemm_mxfp4_packed") &&
+      hip_ok(hipStreamSynchronize(s), "hipStreamSynchronize") &&
+      hip_ok(hipMemcpy(c.data(), dC, c.size() * sizeof(float), hipMemcpyDeviceToHost), "copy C"))
+    rc = 0;
+  if (s) (void)hipStreamDestroy(s);
+  for (void* p : {dX, dT, dWc, dWs, dAc, dAs, dBc, dBs, dC}) (void)hipFree(p);
+  if (rc != 0) return rc;
+  std::FILE* out = std::fopen(out_path, "wb");
+  if (!out) {
+    std::fprintf(stderr, "cannot write %s\n", out_path);
+    return 2;
+  }
+  ok = std::fwrite("WUSHOUTG", 1, 8, out) == 8 && std::fwrite(c.data(), sizeof(float), c.size(), out) == c.size();
+  ok = (std::fclose(out) == 0) && ok;
+  if (!ok) {
+    std::fprintf(stderr, "write failed\n");
+    return 2;
+  }
+  return 0;
+}
+
 int main(int argc, char** argv) {
   if (argc != 3) {
     std::fprintf(stderr, "usage: %s in.bin out.bin\n", argv[0]);
@@ -59,11 +128,13 @@ int main(int argc, char** argv) {
     std::fprintf(stderr, "cannot open %s\n", argv[1]);
     return 2;
   }
-  char magic[8];
+  char magic[8] = {};
+  const bool got_magic = read_into(in, magic, 8);
+  if (got_magic && std::memcmp(magic, "WUSHGEM1", 8) == 0) return run_gemm(in, argv[2]);
   int32_t fmt = 0, G = 0;
   int64_t M = 0, K = 0;
   float g_static = 0.0f;
-  bool ok = read_into(in, magic, 8) && std::memcmp(magic, "WUSHCLI1", 8) == 0 && read_into(in, &fmt, 1) &&
+  bool ok = got_magic && std::memcmp(magic, "WUSHCLI1", 8) == 0 && read_into(in, &fmt, 1) &&
             read_into(in, &G, 1) && read_into(in, &M, 1) && read_into(in, &K, 1) && read_into(in, &g_static, 1);
   ok = ok && (fmt == 0 || fmt == 1 || fmt == 2) && (G == (fmt == 1 ? 16 : 32)) && M >= 0 && K > 0 && K % G == 0 &&
        M <= (int64_t)1 << 24 && K <= (int64_t)1 << 20;

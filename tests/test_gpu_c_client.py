@@ -83,6 +83,49 @@ def test_client_empty_batch(tmp_path):
     assert codes.shape == (0, 128) and scales.shape == (0, 8)
 
 
+def test_client_eq10_forward(tmp_path):
+    """The whole forward from C: wush_quant_mxfp4_packed on the activations,
+    wush_gemm_pack_b on MXFP4 weights, wush_gemm_mxfp4_packed.  C is
+    compared with the oracle's quantize-then-multiply on the same inputs.
+    At least 99% of the entries must lie within the fp32 accumulation bound,
+    and every entry within it plus one E2M1 step of one activation element
+    (a code that differs at a rounding tie moves a whole row of C)."""
+    from oracle import gemm
+    from synthetic.gemm_operands import gen_mx_operand
+
+    assert os.path.exists(EXE), "C client not built: run __graft_entry__.build()"
+    M, N, K = 200, 300, 512
+    _, tb = cases.transforms("tiny_mxfp4", 32)
+    tb = np.concatenate([tb, tb])  # 16 blocks for K = 512
+    xb = np.concatenate([cases.x_rows("tiny_mxfp4", 0, 128), cases.x_rows("tiny_mxfp4", 0, 72)])
+    xb = np.ascontiguousarray(np.concatenate([xb, xb], axis=1))
+    wc, ws = gen_mx_operand(N, K, seed=77, scale_lo=118, scale_hi=126)
+    inp, out = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(inp, "wb") as f:
+        f.write(b"WUSHGEM1" + struct.pack("<qqq", M, N, K))
+        for arr in (xb.astype(np.uint16), tb.astype(np.uint16), wc, ws):
+            f.write(np.ascontiguousarray(arr).tobytes())
+    print("client: gemm M=%d N=%d K=%d" % (M, N, K), flush=True)
+    r = subprocess.run([EXE, str(inp), str(out)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, "client exit %d: %s" % (r.returncode, r.stderr)
+    raw = out.read_bytes()
+    assert raw[:8] == b"WUSHOUTG" and len(raw) == 8 + 4 * M * N
+    C = np.frombuffer(raw, np.float32, M * N, 8).reshape(M, N).astype(np.float64)
+    ac, asc = quant.run_path("mxfp4", xb, tb)
+    ref = gemm.gemm_mxfp4_ref(ac, asc, wc, ws)
+    absref = gemm.gemm_mxfp4_abs_ref(ac, asc, wc, ws)
+    err = np.abs(C - ref)
+    tol = (K - 1) * 2.0**-24 * absref
+    # One E2M1 step is at most 2 (between 4 and 6) times the block's scale.
+    step_a = 2.0 * np.exp2(np.repeat(asc.astype(np.float64) - 127.0, 32, axis=1))  # [M][K]
+    w = np.abs(quant.dequant_mxfp4(wc, ws))
+    one_step = (step_a[:, None, :] * w[None, :, :]).max(axis=2)  # [M][N]
+    inside = np.mean(err <= tol)
+    print("entries within the fp32 bound: %.4f" % inside, flush=True)
+    assert inside >= 0.99
+    assert np.all(err <= tol + one_step)
+
+
 def test_client_reports_bad_shape(tmp_path):
     # K not a multiple of G never reaches the library: the client rejects
     # the header.  A K the library rejects (MXFP4 needs K % 32 == 0 and the
