@@ -85,7 +85,10 @@ def parse():
     ap.add_argument("--workload", default="llama8b_mxfp4",
                     help="llama8b_mxfp4 (default), downproj_mxfp4, nvfp4, int4, tiny_mxfp4")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: > 2x MALL)")
-    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--mode", choices=["eager", "graph"], default="eager",
+                    help="timed steps as back-to-back launches (eager, default) or as one HIP graph; a graph "
+                         "replay costs about 10 us more to start than the first eager launch, which is 2%% of "
+                         "a 20-step run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the hot-cache and device-copy context runs (for counter profiles)")
@@ -718,9 +721,15 @@ def main():
     ptrs = [(X.data_ptr(), T.data_ptr(), c.data_ptr(), s.data_ptr()) for X, T, c, s in sets]
     quant_fn = lib.wush_quant
 
+    # The launch stream: the device's current stream, looked up once for
+    # eager launches, and per call while a graph is being captured.
+    eager_stream = torch.cuda.current_stream().cuda_stream
+    capturing = [False]
+
     def launch(i):
         xp, tp, cp, sp = ptrs[i % n_sets]
-        st = quant_fn(fmt_id, xp, tp, M, K, gs_ptr, cp, sp, None, torch.cuda.current_stream().cuda_stream)
+        strm = torch.cuda.current_stream().cuda_stream if capturing[0] else eager_stream
+        st = quant_fn(fmt_id, xp, tp, M, K, gs_ptr, cp, sp, None, strm)
         if st:
             _lib.check(st, "wush_quant")
 
@@ -740,28 +749,35 @@ def main():
     torch.cuda.synchronize()
     kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
 
-    # Timed region: exactly K steps back to back.  In graph mode the K steps
-    # are one HIP graph (each launch on the next buffer set), so neither host
-    # launch cost nor graph-to-graph gaps gate the device.
+    # Timed region: exactly K steps back to back, each launch on the next
+    # buffer set.  Eager launches (the default) keep the device busy: the
+    # host enqueues a launch in a few microseconds, the kernel runs about
+    # ten.  In graph mode the K steps are one HIP graph.
     if args.mode == "graph":
         cap = torch.cuda.Stream()
 
         def capture(n, first=0):
             g = torch.cuda.CUDAGraph()
+            capturing[0] = True
             with torch.cuda.graph(g, stream=cap):
                 for i in range(first, first + n):
                     launch(i)
+            capturing[0] = False
             return g
 
         g_timed = capture(args.steps)
         g_timed.replay()  # uploads the graph; not counted as steps
         torch.cuda.synchronize()
-    # Warmup: W untimed steps, directly before the timed region.
+    # Warmup: W untimed steps, directly before the timed region, on the
+    # buffer sets that precede set 0 in the rotation, so the timed steps
+    # continue the rotation and each reads a set that left the caches
+    # n_sets - 1 steps earlier.
+    wfirst = (-args.warmup) % n_sets
     if args.mode == "graph" and args.warmup:
-        wg = capture(args.warmup, args.steps)
+        wg = capture(args.warmup, wfirst)
         wg.replay()
     else:
-        for i in range(args.warmup):
+        for i in range(wfirst, wfirst + args.warmup):
             launch(i)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -792,9 +808,11 @@ def main():
     def graph_ms(fn, n, reps):
         cap = torch.cuda.Stream()
         g = torch.cuda.CUDAGraph()
+        capturing[0] = True
         with torch.cuda.graph(g, stream=cap):
             for i in range(n):
                 fn(i)
+        capturing[0] = False
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -805,9 +823,20 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (n * reps)
 
-    hot_ms = copy_ms = float("nan")
+    hot_ms = copy_ms = packed_ms = float("nan")
     if not args.no_context:
         hot_ms, copy_ms = context_runs(graph_ms, launch, sets, n_sets, nbytes, M, K, dev)
+        # The same codes and scales in the GEMM's packed operand layout
+        # (wush_quant_mxfp4_packed), cold, on the same sets; its buffers are
+        # the sets' own when M is a multiple of 128.
+        if fmt == "mxfp4" and K % 256 == 0 and M % 128 == 0:
+            def launch_packed(i):
+                xp, tp, cp, sp = ptrs[i % n_sets]
+                strm = torch.cuda.current_stream().cuda_stream
+                _lib.check(lib.wush_quant_mxfp4_packed(xp, tp, M, K, cp, sp, strm), "wush_quant_mxfp4_packed")
+
+            packed_ms = graph_ms(launch_packed, n_sets * 4, 4)
+            row_major_ms = graph_ms(launch, n_sets * 4, 4)
 
     # NVFP4 with its per-tensor scale computed in the same step: the AbsMax
     # pre-pass (transform of the whole tensor, max |y|, g = max / (6 * 448))
@@ -891,6 +920,11 @@ def main():
         "device_copy_cold": {"bytes_read_plus_written": 2 * half, "us": round(copy_ms * 1e3, 3),
                              "GBps": round(2 * half / (copy_ms * 1e-3) / 1e9, 2)},
     }
+    if out["context"] is not None and packed_ms == packed_ms:
+        out["context"]["gemm_packed_layout_cold"] = {
+            "entry": "wush_quant_mxfp4_packed", "us": round(packed_ms * 1e3, 3),
+            "GBps": round(nbytes / (packed_ms * 1e-3) / 1e9, 2),
+            "row_major_same_graphs_us": round(row_major_ms * 1e3, 3)}
     if prepass is not None:
         out["context"]["nvfp4_with_absmax_prepass"] = prepass
     if not args.no_cpu_baseline:
