@@ -351,12 +351,17 @@ def compare_transforms(args) -> None:
     fmt_id = _lib.FMT[fmt]
     cap = torch.cuda.Stream()
     graphs = {}
+    # Each bank's tensor scale stays referenced while its graph exists:
+    # torch.cuda.graph() empties the allocator cache at every capture, so a
+    # dropped tensor could be unmapped under an earlier graph.
+    g_keep = []
     for ti, name in enumerate(TRANSFORMS):
         if fmt == "nvfp4":
             g = torch.zeros(1, dtype=torch.float32, device=dev)
             wush.nvfp4_global_scale(X0, banks[name], out=g)
         else:
             g = gscale
+        g_keep.append(g)
 
         def launch(i, name=name, g=g, cnt=None):
             c, s = outs[i % n_sets]

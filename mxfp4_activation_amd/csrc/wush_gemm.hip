@@ -202,6 +202,16 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
     s_step = 8 * 128;
   }
   const int s_dst = (s_is_a ? Gm::kOffSA : Gm::kOffSB) + 128 * TM * (wave & 3);
+  // Both operands packed: a tile's scales for one step are 8 BT contiguous
+  // bytes in global memory and in LDS, so one 16-byte-per-lane copy (lanes
+  // below 32 TM) moves them.  Waves ks % 4 (A) and 4 + ks % 4 (B) take turns,
+  // two copies per workgroup and step instead of eight 4-byte ones.
+  constexpr bool kScale16 = PACKED_A && PACKED_B;
+  glb_u8* const s16_src = kScale16 ? (glb_u8*)(s_is_a ? g.a_scales : g.b_scales) +
+                                         (s_is_a ? pa_rows : pt_rows) * row_scales +
+                                         512 * (s_is_a ? pa_half : p_half) + 16 * lane
+                                   : nullptr;
+  const int s16_dst = s_is_a ? Gm::kOffSA : Gm::kOffSB;
 
   // Step ks lives in ring stage ks % kStages.
   const uint32_t wave_u = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
@@ -213,7 +223,12 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
       dma16(a_src[q] + kc * (PACKED_A ? kPackStep : kRowB), st + 1024 * (TM * wave_u + q));
       dma16(b_src[q] + kc * (PACKED_B ? kPackStep : kRowB), st + Gm::kOffB + 1024 * (TM * wave_u + q));
     }
-    if (s_lane) dma4(s_src + kc * s_step, st + (uint32_t)__builtin_amdgcn_readfirstlane(s_dst));
+    if (kScale16) {
+      if ((int)(wave_u & 3) == (ks & 3) && s_lane)
+        dma16(s16_src + kc * 1024, st + (uint32_t)__builtin_amdgcn_readfirstlane(s16_dst));
+    } else if (s_lane) {
+      dma4(s_src + kc * s_step, st + (uint32_t)__builtin_amdgcn_readfirstlane(s_dst));
+    }
   };
 
   f32x16 acc[TM][TM];
@@ -283,7 +298,9 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp4_kernel(GemmArgs g) {
   // fragments every wave read and consumed (in mfma) before this barrier;
   // only step ks - 1's reads may still be in flight when the barrier
   // passes, and its stage is a different one.
-  constexpr int LPS = Gm::kLoadsPerStep;
+  // With kScale16 a wave issues a scale copy on one step in four; counting
+  // only its 2 TM code copies per step waits for at most one later copy too.
+  constexpr int LPS = kScale16 ? 2 * TM : Gm::kLoadsPerStep;
   auto sync = [&](int ks) {
     const int later = min(Gm::kAhead - 1, nk - 1 - ks);  // steps issued after ks
     switch (later) {
