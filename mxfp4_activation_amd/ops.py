@@ -25,6 +25,9 @@ def _check_x_t(X: torch.Tensor, T: torch.Tensor, G: int) -> Tuple[int, int]:
         raise TypeError("X and T must be bfloat16")
     if not (X.is_cuda and T.is_cuda):
         raise ValueError("X and T must be device tensors")
+    if T.device != X.device or X.device.index != torch.cuda.current_device():
+        raise ValueError("X and T must be on the current device (X on %s, T on %s, current cuda:%d)"
+                         % (X.device, T.device, torch.cuda.current_device()))
     if X.dim() != 2:
         raise ValueError("X must be [M, K]")
     M, K = X.shape
