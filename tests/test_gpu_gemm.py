@@ -200,9 +200,10 @@ def test_pack_b_layout(N, K):
 @pytest.mark.parametrize("M,N,K", [(7, 33, 256), (64, 200, 512), (77, 390, 4352), (1000, 3000, 2304),
                                    (1000, 5096, 512), (1024, 1024, 4096), (1024, 4096, 4096)])
 def test_packed_b_matches_unpacked(M, N, K):
-    """The GEMM with packed weights gives the unpacked GEMM's result bit for
-    bit: 64 x 64 tiles that are second halves of packed 128-row tiles, ragged
-    edges, the split last wave, and whole layer shapes."""
+    """The GEMM with packed weights, and with both operands packed, gives the
+    unpacked GEMM's result bit for bit in fp32 and bf16: 64 x 64 tiles that
+    are second halves of packed 128-row tiles, ragged edges, the split last
+    wave, and whole layer shapes."""
     from mxfp4_activation_amd import ops
 
     print("packed", M, N, K, flush=True)
@@ -217,11 +218,13 @@ def test_packed_b_matches_unpacked(M, N, K):
     # the same layout the packed quantizer does).
     pa = ops.gemm_pack_b(a, a_s)
     c5 = ops.gemm_mxfp4_packed(pa, pb, out_dtype=torch.float32)
+    c6 = ops.gemm_mxfp4_packed(pa, pb, out_dtype=torch.bfloat16)
     c4 = ops.gemm_mxfp4(a, a_s, b, b_s, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
     assert torch.equal(c3.view(torch.int16), c4.view(torch.int16))
     assert torch.equal(c1.view(torch.int32), c5.view(torch.int32))
+    assert torch.equal(c4.view(torch.int16), c6.view(torch.int16))
     if M * N * K <= 1 << 31:
         ref = gemm.gemm_mxfp4_ref(ac, asc, bc, bsc)
         absref = gemm.gemm_mxfp4_abs_ref(ac, asc, bc, bsc)
