@@ -24,6 +24,7 @@ baseline.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -785,6 +786,9 @@ def main():
         for i in range(wfirst, wfirst + args.warmup):
             launch(i)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # No garbage collection pass may stall the host between eager launches.
+    gc_was_on = gc.isenabled()
+    gc.disable()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
@@ -796,6 +800,8 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    if gc_was_on:
+        gc.enable()
     ms_total = t_start.elapsed_time(t_end)
     ms_per_step = ms_total / args.steps
 
