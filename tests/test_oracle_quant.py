@@ -158,6 +158,38 @@ def test_transform_cyclic_shift_not_transposed():
         np.testing.assert_array_equal(y[:, c * G:(c + 1) * G], np.roll(blk, -s, axis=1))
 
 
+def test_transform_f64_shift_and_brute_force():
+    """The float64 reference transform (unrounded T): the same cyclic shift
+    as above moves x_(k+s_c) into y_k, and on a small case with a general T
+    every output is within float64 summation error of the exact rational
+    sum."""
+    rng = np.random.default_rng(2)
+    G, C, M = 16, 3, 4
+    X = rng.standard_normal((M, C * G))
+    x_bits = _bits(X)
+    xf = codecs.bf16_bits_to_f32(x_bits).astype(np.float64)
+    T = np.zeros((C, G, G))
+    shifts = [2, 7, 15]
+    for c, s in enumerate(shifts):
+        for k in range(G):
+            T[c, k, (k + s) % G] = 1.0
+    y = quant.transform_f64(x_bits, T)
+    for c, s in enumerate(shifts):
+        np.testing.assert_array_equal(y[:, c * G:(c + 1) * G], np.roll(xf[:, c * G:(c + 1) * G], -s, axis=1))
+    # General T (float64 entries, not bf16): within float64 summation error
+    # of the exact rational sum, (G + 2) 2^-53 sum |T x| (G - 1 additions and
+    # one product rounding per term).  A dropped term, a wrong index or a
+    # transposed T is off by a whole term.
+    Tg = rng.standard_normal((C, G, G))
+    y = quant.transform_f64(x_bits, Tg)
+    for m in range(M):
+        for c in range(C):
+            for k in range(G):
+                terms = [Fraction(float(Tg[c, k, j])) * Fraction(float(xf[m, c * G + j])) for j in range(G)]
+                exact, mag = sum(terms), sum(abs(t) for t in terms)
+                assert abs(Fraction(float(y[m, c * G + k])) - exact) <= (G + 2) * mag / 2**53
+
+
 def test_identity_transform_is_plain_mxfp4():
     """T = I: the path is plain OCP MXFP4 of X.  Checked element-wise against
     the round trip: every dequantized value is the grid level nearest x."""
